@@ -1,0 +1,361 @@
+/*
+ * Plain, slow, fp64 CPU reference for absorbed-query MLA decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call this file:
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * load it.  It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (one query token per request, all heads share one latent
+ * KV head):
+ *
+ *   vLLM API docs, vllm.model_executor.layers.attention.mla_attention, module
+ *   docstring, section "Data-Movement Friendly Approach (i.e. forward_mqa)":
+ *   attention whose query is cat[ql_nope, q_pe] (width Lkv + R = 576), whose
+ *   keys are the cached rows cat[kv_c, k_pe] (width 576) and whose values are
+ *   kv_c itself (the first Lkv = 512 columns of the same rows).
+ *
+ *   Model-Optimizer docs, modelopt.torch.kernels.quantization.attention.mla,
+ *   mla_attention_decode, "Parameters" and "Returns": q [batch, num_heads,
+ *   576]; latent_cache [num_blocks, page_size, 576]; block_table
+ *   [batch, max_blocks_per_seq]; b_seq_len [batch]; softmax_scale is a
+ *   required argument; the result is out [batch, num_heads, 512] and the
+ *   natural-log LSE [batch, num_heads].
+ *
+ *   vllm-cpu 0.8.5.post2, vllm/v1/attention/backends/mla/common.py,
+ *   get_kv_cache_shape: the cache is (num_blocks, block_size, head_size) with
+ *   a single KV head.
+ *
+ * For one (request b, head n) with L = seq_lens[b] > 0 and
+ * K[t] = row t of the request, found through the page table:
+ *
+ *   s_t   = softmax_scale * sum_d q[b,n,d] * K[t,d]          (d < Dqk)
+ *   lse   = log(sum_t exp(s_t))              (natural log, computed stably)
+ *   out_l = sum_t exp(s_t - lse) * K[t,l]                    (l < Dv)
+ *
+ * L == 0 gives out = 0 and lse = -inf: a zero output with an -inf LSE is the
+ * state that carries no weight in an LSE merge (vLLM API docs,
+ * neutralize_empty_context_partials).
+ *
+ * Cache element decoding:
+ *   - bf16: the value is the binary32 number whose upper 16 bits are the
+ *     stored bits (bfloat16 is defined as truncated binary32).
+ *   - fp8: OCP 8-bit floating point, E4M3 "FN" variant (exponent bias 7, no
+ *     infinities, S.1111.111 is NaN, max normal 448), multiplied by the
+ *     per-tensor cache scale: the cache stores latent / scale and readers
+ *     multiply the scale back into both the latent and k_pe (raon-1-mini
+ *     mla_attention.py, the fp8 insert and the dequantize_context_latent
+ *     comments).
+ *
+ * Every accumulation is a plain left-to-right fp64 loop; nothing is split,
+ * blocked or fused.  Requests are processed one (b, n) row at a time; rows are
+ * handed to worker threads, which changes nothing in the arithmetic of a row.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element decoding -------------------------------------------------- */
+
+double oracle_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP E4M3 (FN): sign 1 bit, exponent 4 bits (bias 7), mantissa 3 bits.
+ * exponent 0: subnormal, value = (m / 8) * 2^-6.
+ * otherwise:  value = (1 + m / 8) * 2^(e - 7); e = 15, m = 7 is NaN. */
+double oracle_e4m3fn_to_double(uint8_t bits)
+{
+    int sign = bits >> 7;
+    int e = (bits >> 3) & 0xF;
+    int m = bits & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* ---- problem description ----------------------------------------------- */
+
+typedef struct {
+    int B, N, Dqk, Dv, page_size, max_blocks, num_blocks;
+    int cache_is_fp8;
+    const double *q;          /* [B, N, Dqk], already exact doubles        */
+    const void *cache;        /* [num_blocks, page_size, Dqk] bf16 or fp8  */
+    double cache_scale;       /* fp8 only; 1 for bf16                       */
+    const int32_t *block_table; /* [B, max_blocks]                          */
+    const int32_t *seq_lens;  /* [B]                                        */
+    double softmax_scale;
+} oracle_problem;
+
+/* Element d of token t of request b, or NaN when the page table or the
+ * length does not describe a valid row (the caller has already rejected
+ * such inputs, so this only guards against misuse). */
+static double cache_elem(const oracle_problem *p, int b, int64_t t, int d)
+{
+    int64_t page = t / p->page_size;
+    int64_t row = t % p->page_size;
+    int32_t blk = p->block_table[(int64_t)b * p->max_blocks + page];
+    int64_t idx = ((int64_t)blk * p->page_size + row) * p->Dqk + d;
+    if (p->cache_is_fp8)
+        return oracle_e4m3fn_to_double(((const uint8_t *)p->cache)[idx]) *
+               p->cache_scale;
+    return oracle_bf16_to_double(((const uint16_t *)p->cache)[idx]);
+}
+
+/* Attention of query row (b, n) over tokens [t0, t1) of request b.
+ * Writes Dv outputs and the natural-log LSE.  An empty span gives the
+ * neutral state (0, -inf).  `scores` must hold t1 - t0 doubles. */
+static void attend_span(const oracle_problem *p, int b, int n, int64_t t0,
+                        int64_t t1, double *scores, double *out, double *lse)
+{
+    const double *qv = p->q + ((int64_t)b * p->N + n) * p->Dqk;
+    int64_t L = t1 - t0;
+    for (int l = 0; l < p->Dv; ++l)
+        out[l] = 0.0;
+    if (L <= 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    /* scores s_t = scale * <q, K[t]> over all Dqk columns */
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < L; ++t) {
+        double dot = 0.0;
+        for (int d = 0; d < p->Dqk; ++d)
+            dot += qv[d] * cache_elem(p, b, t0 + t, d);
+        scores[t] = p->softmax_scale * dot;
+        if (scores[t] > mx)
+            mx = scores[t];
+    }
+    /* Z = sum_t exp(s_t - max);  lse = max + log Z */
+    double Z = 0.0;
+    for (int64_t t = 0; t < L; ++t)
+        Z += exp(scores[t] - mx);
+    *lse = mx + log(Z);
+    /* out = sum_t softmax_t * V[t], V = first Dv columns of the row */
+    for (int64_t t = 0; t < L; ++t) {
+        double w = exp(scores[t] - mx) / Z;
+        for (int l = 0; l < p->Dv; ++l)
+            out[l] += w * cache_elem(p, b, t0 + t, l);
+    }
+}
+
+/* ---- input validation --------------------------------------------------- */
+
+/* Returns 0 when every row the oracle would touch is addressable. */
+static int check_problem(const oracle_problem *p)
+{
+    if (p->B < 0 || p->N <= 0 || p->Dqk <= 0 || p->Dv <= 0 || p->Dv > p->Dqk ||
+        p->page_size <= 0 || p->max_blocks < 0 || p->num_blocks <= 0)
+        return 1;
+    for (int b = 0; b < p->B; ++b) {
+        int64_t L = p->seq_lens[b];
+        if (L < 0 || L > (int64_t)p->max_blocks * p->page_size)
+            return 2;
+        int64_t pages = (L + p->page_size - 1) / p->page_size;
+        for (int64_t i = 0; i < pages; ++i) {
+            int32_t blk = p->block_table[(int64_t)b * p->max_blocks + i];
+            if (blk < 0 || blk >= p->num_blocks)
+                return 3;
+        }
+    }
+    return 0;
+}
+
+/* ---- threaded driver over (b, n) rows ----------------------------------- */
+
+typedef struct {
+    const oracle_problem *p;
+    int n_rows;
+    const int32_t *row_b, *row_n;
+    const int64_t *span_t0, *span_t1; /* NULL: the whole sequence */
+    double *out, *lse;
+    int next;                          /* shared work counter */
+    pthread_mutex_t lock;
+} oracle_job;
+
+static void *worker(void *arg)
+{
+    oracle_job *job = (oracle_job *)arg;
+    const oracle_problem *p = job->p;
+    double *scores = NULL;
+    int64_t cap = 0;
+    for (;;) {
+        pthread_mutex_lock(&job->lock);
+        int r = job->next++;
+        pthread_mutex_unlock(&job->lock);
+        if (r >= job->n_rows)
+            break;
+        int b = job->row_b[r], n = job->row_n[r];
+        int64_t t0 = job->span_t0 ? job->span_t0[r] : 0;
+        int64_t t1 = job->span_t1 ? job->span_t1[r] : p->seq_lens[b];
+        if (t1 - t0 > cap) {
+            free(scores);
+            cap = t1 - t0;
+            scores = (double *)malloc((size_t)cap * sizeof(double));
+            if (!scores) {
+                cap = 0;
+                job->lse[r] = NAN; /* out of memory: poison the row */
+                continue;
+            }
+        }
+        attend_span(p, b, n, t0, t1, scores, job->out + (int64_t)r * p->Dv,
+                    job->lse + r);
+    }
+    free(scores);
+    return NULL;
+}
+
+static int run_rows(const oracle_problem *p, int n_rows, const int32_t *row_b,
+                    const int32_t *row_n, const int64_t *t0, const int64_t *t1,
+                    double *out, double *lse, int nthreads)
+{
+    oracle_job job;
+    job.p = p;
+    job.n_rows = n_rows;
+    job.row_b = row_b;
+    job.row_n = row_n;
+    job.span_t0 = t0;
+    job.span_t1 = t1;
+    job.out = out;
+    job.lse = lse;
+    job.next = 0;
+    pthread_mutex_init(&job.lock, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, worker, &job) == 0)
+            ++started;
+    worker(&job);
+    for (int i = 0; i < started; ++i)
+        pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&job.lock);
+    return 0;
+}
+
+/* ---- exported entry points ---------------------------------------------- */
+
+/* Full decode, or a chosen list of (b, n) rows.
+ * n_rows < 0: every row, in (b, n) order, out is [B, N, Dv] and lse [B, N].
+ * n_rows >= 0: rows (row_b[i], row_n[i]); out is [n_rows, Dv], lse [n_rows].
+ * Returns 0, or a nonzero code when the inputs address rows outside the
+ * cache (the oracle refuses them rather than guessing). */
+int oracle_mla_decode(int B, int N, int Dqk, int Dv, int page_size,
+                      int max_blocks, int num_blocks, int cache_is_fp8,
+                      const double *q, const void *cache, float cache_scale,
+                      const int32_t *block_table, const int32_t *seq_lens,
+                      float softmax_scale, int n_rows, const int32_t *row_b,
+                      const int32_t *row_n, double *out, double *lse,
+                      int nthreads)
+{
+    oracle_problem p = {B, N, Dqk, Dv, page_size, max_blocks, num_blocks,
+                        cache_is_fp8, q, cache,
+                        cache_is_fp8 ? (double)cache_scale : 1.0,
+                        block_table, seq_lens, (double)softmax_scale};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    if (n_rows < 0) {
+        int total = B * N;
+        int32_t *rb = (int32_t *)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
+        int32_t *rn = (int32_t *)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
+        if (!rb || !rn) {
+            free(rb);
+            free(rn);
+            return 10;
+        }
+        for (int b = 0; b < B; ++b)
+            for (int n = 0; n < N; ++n) {
+                rb[b * N + n] = b;
+                rn[b * N + n] = n;
+            }
+        run_rows(&p, total, rb, rn, NULL, NULL, out, lse, nthreads);
+        free(rb);
+        free(rn);
+        return 0;
+    }
+    for (int i = 0; i < n_rows; ++i)
+        if (row_b[i] < 0 || row_b[i] >= B || row_n[i] < 0 || row_n[i] >= N)
+            return 4;
+    run_rows(&p, n_rows, row_b, row_n, NULL, NULL, out, lse, nthreads);
+    return 0;
+}
+
+/* Attention of rows (row_b[i], row_n[i]) over token spans [t0[i], t1[i]) of
+ * their requests: the partial state (normalised output, natural-log LSE) of
+ * one KV split.  An empty span gives (0, -inf). */
+int oracle_mla_attend_spans(int B, int N, int Dqk, int Dv, int page_size,
+                            int max_blocks, int num_blocks, int cache_is_fp8,
+                            const double *q, const void *cache,
+                            float cache_scale, const int32_t *block_table,
+                            const int32_t *seq_lens, float softmax_scale,
+                            int n_rows, const int32_t *row_b,
+                            const int32_t *row_n, const int64_t *t0,
+                            const int64_t *t1, double *out, double *lse,
+                            int nthreads)
+{
+    oracle_problem p = {B, N, Dqk, Dv, page_size, max_blocks, num_blocks,
+                        cache_is_fp8, q, cache,
+                        cache_is_fp8 ? (double)cache_scale : 1.0,
+                        block_table, seq_lens, (double)softmax_scale};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    for (int i = 0; i < n_rows; ++i) {
+        if (row_b[i] < 0 || row_b[i] >= B || row_n[i] < 0 || row_n[i] >= N)
+            return 4;
+        if (t0[i] < 0 || t1[i] > seq_lens[row_b[i]])
+            return 5;
+    }
+    run_rows(&p, n_rows, row_b, row_n, t0, t1, out, lse, nthreads);
+    return 0;
+}
+
+/* LSE merge of S partial states per row (the combination that
+ * merge_attn_states performs for two states in the vLLM docs, written for S):
+ *   lse   = log(sum_s exp(lse_s))          (stably, about max_s lse_s)
+ *   out_l = sum_s exp(lse_s - lse) * out_s,l
+ * When every lse_s is -inf the row carries no weight: out = 0, lse = -inf.
+ * part_out is [R, S, Dv], part_lse [R, S]; out [R, Dv], lse [R]. */
+void oracle_merge_states(int R, int S, int Dv, const double *part_out,
+                         const double *part_lse, double *out, double *lse)
+{
+    for (int r = 0; r < R; ++r) {
+        const double *ls = part_lse + (int64_t)r * S;
+        double *o = out + (int64_t)r * Dv;
+        double mx = -INFINITY;
+        for (int s = 0; s < S; ++s)
+            if (ls[s] > mx)
+                mx = ls[s];
+        for (int l = 0; l < Dv; ++l)
+            o[l] = 0.0;
+        if (mx == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double Z = 0.0;
+        for (int s = 0; s < S; ++s)
+            Z += exp(ls[s] - mx);
+        double total = mx + log(Z);
+        lse[r] = total;
+        for (int s = 0; s < S; ++s) {
+            double w = exp(ls[s] - total);
+            const double *os = part_out + ((int64_t)r * S + s) * Dv;
+            for (int l = 0; l < Dv; ++l)
+                o[l] += w * os[l];
+        }
+    }
+}
