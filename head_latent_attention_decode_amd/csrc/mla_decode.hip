@@ -1,0 +1,1193 @@
+// MLA decode for MI355X (gfx950): split-KV absorbed-query attention over a
+// paged latent cache, plus the LSE merge of the split partials.
+//
+// What is computed (vLLM API docs, vllm.model_executor.layers.attention.
+// mla_attention, module docstring, "Data-Movement Friendly Approach (i.e.
+// forward_mqa)"; Model-Optimizer docs, modelopt.torch.kernels.quantization.
+// attention.mla, mla_attention_decode): every head of a request attends with
+// its 576-wide absorbed query over the request's cached rows cat[kv_c, k_pe];
+// the value of a row is its first 512 columns.  Output: out [B, N, 512] and
+// the natural-log LSE [B, N].
+//
+// Design (gfx950, wave64):
+//  * One workgroup per (request, KV split, head group).  All heads of the
+//    group share every KV tile: a tile of rows is fetched from HBM once,
+//    straight into LDS with global_load_lds_dwordx4 (no VGPR staging), and
+//    read from LDS by every wave.
+//  * QK^T runs on bf16 MFMA as S^T = K . Q^T: the K tile (tokens x 576, read
+//    from LDS in its natural row-major layout) is the A operand, the query
+//    fragments held in VGPRs are the B operand, so each wave's heads form the
+//    N dimension and each K fragment read from LDS serves all of them.
+//  * The S^T accumulator layout (head on the lane, tokens in registers) is
+//    exactly the B-operand layout PV needs for P^T, so the softmax output
+//    feeds PV without any cross-lane movement.  PV runs as O^T = V^T . P^T
+//    with V^T read from the same LDS tile by ds_read_b64_tr_b16 (a transposed
+//    LDS read), so the value rows are never copied or transposed in memory.
+//  * Online softmax in the log2 domain with a lazy running maximum: the
+//    accumulators are rescaled only when a tile's maximum exceeds the running
+//    one by more than 2^8, which keeps every weight <= 256 and skips almost
+//    all rescales.  Row maxima and sums use wavefront lane exchanges.
+//  * LDS rows are stored with an XOR swizzle of their 16-byte chunks so that
+//    both the MFMA operand reads and the transposed reads avoid bank
+//    conflicts; the swizzle is applied by choosing which global chunk each
+//    lane fetches, since a direct-to-LDS load writes 64 consecutive slots.
+//  * Workgroup ids are remapped so consecutive work items share an XCD (and
+//    its L2): the splits of one request then reuse its query from L2.
+//  * The split partials (normalised output, LSE) go to a caller workspace and
+//    a second kernel merges them; with one split the first kernel writes the
+//    bf16 output directly.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_decode.h"
+
+namespace {
+
+constexpr int kD = 576;                 // query / row width (Lkv + R)
+constexpr int kDV = 512;                // value / output width (Lkv)
+constexpr int kRowBytes = kD * 2;       // a bf16 row
+constexpr int kRowChunks = kRowBytes / 16;
+constexpr int kSplitUnit = 32;          // split boundaries are multiples of this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.0f;    // log2 headroom before a rescale
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define AS3(ptr) ((LDS_AS uint8_t *)(ptr))
+
+struct Params {
+    const __bf16 *q;            // [B, N, 576]
+    const uint8_t *cache;       // [num_blocks, P, 576] elements
+    const float *cache_scale;   // fp8: one float; bf16: unused
+    const int32_t *block_table; // [B, MB]
+    const int32_t *seq_lens;    // [B]
+    float *part_out;            // [B, N, S, 512]   (split mode)
+    float *part_lse;            // [B, N, S]
+    __bf16 *out;                // [B, N, 512]      (direct mode, S == 1)
+    float *lse;                 // [B, N] or null   (direct mode)
+    float scale_log2;           // softmax_scale * log2(e)
+    int B, N, S, MB, num_blocks, page_shift, HG;
+};
+
+// XOR swizzle of the 16-byte chunks of LDS row r.  Rows r..r+7 then place a
+// given chunk in 8 different bank groups (MFMA operand reads, 8 lanes a
+// pass), and rows 4a..4a+3 place an aligned 32-byte chunk pair in 4 different
+// 32-byte bank groups (transposed reads, 16 lanes a pass).  The XOR stays
+// inside an aligned group of 8 chunks, so it never leaves the 72-chunk row.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Workgroup id -> (request, split, head group).  The hardware deals
+// consecutive workgroup ids round-robin over the 8 XCDs; when the grid is a
+// multiple of 8 the remap gives each XCD a contiguous range of work items.
+__device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int &hg)
+{
+    int i = blockIdx.x;
+    const int G = gridDim.x;
+    if ((G & 7) == 0)
+        i = (i & 7) * (G >> 3) + (i >> 3);
+    hg = i % p.HG;
+    const int bs = i / p.HG;
+    s = bs % p.S;
+    b = bs / p.S;
+}
+
+// Token range [t0, t1) of split s of request b.  The chunk length is
+// ceil(L / S) rounded up to kSplitUnit, a function of (L, S) only.
+__device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &t0, int &t1)
+{
+    const long long cap = (long long)p.MB << p.page_shift;
+    long long L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const long long per = (L + p.S - 1) / p.S;
+    const long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
+    const long long a = (long long)s * C;
+    const long long e = a + C;
+    t0 = (int)(a < L ? a : L);
+    t1 = (int)(e < L ? e : L);
+}
+
+__device__ __forceinline__ int clamp_block(int blk, int num_blocks)
+{
+    return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
+// left at their maximum so they are not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One direct-to-LDS load: lane i's 16 bytes at `src` land at LDS byte
+// address dst + 16 * i (dst is wave-uniform and goes to M0).  Issued as
+// inline assembly so the compiler does not track it: the compiler cannot tell
+// which LDS stage a load targets and would otherwise wait for every load in
+// flight before each LDS read.  Completion is awaited explicitly with
+// wait_vmcnt; the kernels issue no other vector-memory operations while
+// tiles are in flight.
+__device__ __forceinline__ void dma16(const void *src, LDS_AS void *dst)
+{
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(src)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b)
+{
+    f32x2 v = {a, b};
+    return __builtin_convertvector(v, bf16x2);
+}
+
+__device__ __forceinline__ float bf16_round(float x)
+{
+    return (float)(__bf16)x;
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations
+// (lgkmcnt(0): its ds_writes have landed and are visible to the other waves
+// after the barrier), not for its vector-memory operations: __syncthreads()
+// would also wait for every direct-to-LDS tile load in flight, including the
+// prefetched ones.  Tile loads are made visible by an explicit wait_vmcnt
+// before the barrier.  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ bool wave_any(bool c)
+{
+    return __builtin_amdgcn_ballot_w64(c) != 0;
+}
+
+// ---------------------------------------------------------------------------
+// fp8 (E4M3 "FN") cache support.  Rows are staged in LDS as bytes and widened
+// to bf16 before the MFMA reads them; E4M3 -> bf16 is exact (3 mantissa bits,
+// exponents inside bf16's range), so the only rounding is the fp32 MFMA
+// accumulation.  The per-tensor scale is folded into the softmax scale and
+// into the final normalisation.
+// ---------------------------------------------------------------------------
+constexpr int kRowBytes8 = kD;                  // an fp8 row: 576 bytes
+constexpr int kRowChunks8 = kRowBytes8 / 16;    // 36
+
+// 4 E4M3 bytes (byte 0 first) -> 4 bf16 values packed as two dwords
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned v)
+{
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// ===========================================================================
+// 128 heads per workgroup: 8 waves (two per SIMD), 32-token tiles shared by
+// all waves through an LDS ring.
+//   wave w = (g, c), g = w / 2 picks a group of 32 heads, c = w % 2 a half.
+//   QK^T: the wave scores heads 32g + 16c .. +16 over all 32 tokens
+//         (v_mfma_f32_16x16x32_bf16, S^T = K . Q^T, 72 VGPRs of query).
+//   PV:   the wave accumulates all 32 heads of group g over output columns
+//         256c .. 256c+255 (v_mfma_f32_32x32x16_bf16, O^T = V^T . P^T, 128
+//         accumulator registers).
+// The two waves of a group exchange their bf16 probabilities and rescale
+// factors through LDS, so each K fragment read from LDS serves 16 heads and
+// each V fragment 32 heads, while a wave keeps only 16 heads of query and
+// half of the output columns in registers.
+// bf16 cache: a 4-stage ring of bf16 tiles filled by direct-to-LDS loads.
+// fp8 cache: 3 staging buffers of fp8 tiles (direct-to-LDS loads) and 2 bf16
+// stages the workgroup converts them into, one tile ahead of the compute.
+// ===========================================================================
+constexpr int kT32 = 32;                        // tokens per tile
+constexpr int kStage32 = kT32 * kRowBytes;      // 36864 bytes (bf16 tile)
+constexpr int kStage8 = kT32 * kRowBytes8;      // 18432 bytes (fp8 tile)
+constexpr int kPbufBytes = 4 * 32 * 32 * 2;     // [group][head][token] bf16
+constexpr int kAbufBytes = 4 * 32 * 4;          // [group][head] float
+
+template <bool kFp8>
+struct H128Layout {
+    static constexpr int kBf16Stages = kFp8 ? 2 : 4;
+    static constexpr int kStaging = kBf16Stages * kStage32;          // fp8 staging offset
+    static constexpr int kPbuf = kStaging + (kFp8 ? 3 * kStage8 : 0);
+    static constexpr int kAbuf = kPbuf + kPbufBytes;
+    static constexpr int kTotal = kAbuf + kAbufBytes;
+};
+static_assert(H128Layout<false>::kTotal <= 160 * 1024, "LDS budget");
+static_assert(H128Layout<true>::kTotal <= 160 * 1024, "LDS budget");
+
+// bf16 tile: 36 DMA instructions; wave w takes i = w, w+8, ... (5 for waves
+// 0-3, 4 for waves 4-7).  Instruction i fills LDS chunks [64i, 64i+64) of the
+// tile: rows of the half h = i / 18 (rows 16h .. 16h+15), which lie in one
+// page.  Logical chunk c of row r is stored at chunk c ^ swz(r).
+__device__ __forceinline__ void issue_tile32(const Params &p, LDS_AS uint8_t *stage, int w,
+                                             int lane, int b, int tile_start, int t_end)
+{
+    const int last = t_end - 1;
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int first = tile_start + 16 * h;
+        first = first < last ? first : last;
+        const int blk = clamp_block(p.block_table[(long long)b * p.MB + (first >> p.page_shift)],
+                                    p.num_blocks);
+        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes;
+    }
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int i = w + 8 * m;
+        if (i < 36) {
+            const int q = i * 64 + lane;
+            const int r = q / kRowChunks;
+            int tok = tile_start + r;
+            tok = tok < last ? tok : last;
+            const int c = (q % kRowChunks) ^ swz(r);
+            dma16(base[i / 18] + (long long)(tok & pmask) * kRowBytes + c * 16, stage + i * 1024);
+        }
+    }
+}
+
+// fp8 tile: 18 DMA instructions (3 for waves 0-1, 2 for waves 2-7) into an
+// unswizzled staging buffer of 576-byte rows; instruction i covers rows of
+// the half i / 9.
+__device__ __forceinline__ void issue_tile32_fp8(const Params &p, LDS_AS uint8_t *stg, int w,
+                                                 int lane, int b, int tile_start, int t_end)
+{
+    const int last = t_end - 1;
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int first = tile_start + 16 * h;
+        first = first < last ? first : last;
+        const int blk = clamp_block(p.block_table[(long long)b * p.MB + (first >> p.page_shift)],
+                                    p.num_blocks);
+        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const int i = w + 8 * m;
+        if (i < 18) {
+            const int q = i * 64 + lane;
+            const int r = q / kRowChunks8;
+            int tok = tile_start + r;
+            tok = tok < last ? tok : last;
+            dma16(base[i / 9] + (long long)(tok & pmask) * kRowBytes8 + (q % kRowChunks8) * 16,
+                  stg + i * 1024);
+        }
+    }
+}
+
+// Widen a staged fp8 tile into a swizzled bf16 stage: 512 threads, 9 groups
+// of 4 bytes each.
+__device__ __forceinline__ void convert_tile32(const LDS_AS uint8_t *stg, LDS_AS uint8_t *stage,
+                                               int tid)
+{
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int e = m * 512 + tid;
+        const int r = e / 144, c4 = e % 144;
+        const unsigned v = *(const LDS_AS unsigned *)(stg + r * kRowBytes8 + c4 * 4);
+        *(LDS_AS u32x2 *)(stage + r * kRowBytes + ((c4 >> 1) ^ swz(r)) * 16 + (c4 & 1) * 8) =
+            e4m3x4_to_bf16x4(v);
+    }
+}
+
+// Wait until this wave has at most `k` tiles (k = 0, 1, 2) of loads in flight.
+template <bool kFp8>
+__device__ __forceinline__ void wait_tiles128(int w, int k)
+{
+    if (kFp8) {
+        if (w < 2) {
+            if (k >= 2) wait_vmcnt<6>(); else if (k == 1) wait_vmcnt<3>(); else wait_vmcnt<0>();
+        } else {
+            if (k >= 2) wait_vmcnt<4>(); else if (k == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
+        }
+    } else {
+        if (w < 4) {
+            if (k >= 2) wait_vmcnt<10>(); else if (k == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
+        } else {
+            if (k >= 2) wait_vmcnt<8>(); else if (k == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
+        }
+    }
+}
+
+struct State128 {
+    f32x16 o[8];      // O^T: 8 blocks of 32 output columns x 32 heads
+    float m;          // running max (log2) of the wave's 16 QK heads
+    float l;          // this lane's share of their row sums
+};
+
+struct Lane128 {
+    int c, r16, g4, r32, g2;
+    int ko[2];        // QK A-operand offsets (k even / odd)
+    int to[2][2];     // PV transposed-read offsets [half][cb parity]
+};
+
+// One 32-token tile: scores, online softmax, probability exchange, PV.
+// Contains one workgroup barrier (after the probabilities are written).
+__device__ __forceinline__ void tile128(State128 &st, const bf16x8 (&qf)[18],
+                                        const LDS_AS uint8_t *stage, LDS_AS uint8_t *pbuf,
+                                        LDS_AS float *abuf, const Lane128 &ln, float scale_log2,
+                                        int tile_start, int t_end)
+{
+    // ---- S^T[token][head] for 2 blocks of 16 tokens x this wave's 16 heads
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int k = 0; k < 18; ++k) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const bf16x8 a = *(const LDS_AS bf16x8 *)(stage + ln.ko[k & 1] + (k >> 1) * 128 +
+                                                      tb * 16 * kRowBytes);
+            sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k], sc[tb], 0, 0, 0);
+        }
+    }
+    // ---- mask, scale, lazy online softmax of the wave's 16 heads
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = tile_start + 16 * tb + 4 * ln.g4 + i;
+            const float v = sc[tb][i] * scale_log2;
+            x[4 * tb + i] = tok < t_end ? v : -INFINITY;
+            mx = fmaxf(mx, x[4 * tb + i]);
+        }
+    float alpha = 1.0f;
+    if (wave_any(mx > st.m + kLazyRescale)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+        st.m = mnew;
+        st.l *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const bf16x2 p01 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb] - st.m),
+                                     __builtin_amdgcn_exp2f(x[4 * tb + 1] - st.m));
+        const bf16x2 p23 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb + 2] - st.m),
+                                     __builtin_amdgcn_exp2f(x[4 * tb + 3] - st.m));
+        lsum += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+        // P[head 16c + r16][tokens 16tb + 4g4 .. +4]
+        *(LDS_AS bf16x4 *)(pbuf + (16 * ln.c + ln.r16) * 64 + (16 * tb + 4 * ln.g4) * 2) =
+            bf16x4{p01[0], p01[1], p23[0], p23[1]};
+    }
+    st.l += lsum;
+    if (ln.g4 == 0)
+        abuf[16 * ln.c + ln.r16] = alpha;
+    barrier_no_fence();
+
+    // ---- PV: O^T[col][head] += V^T . P^T for the group's 32 heads
+    const float al = abuf[ln.r32];
+    if (wave_any(al != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+            st.o[cb] *= al;
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        pf[kk] = *(const LDS_AS bf16x8 *)(pbuf + ln.r32 * 64 + (16 * kk + 8 * ln.g2) * 2);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4 *)(stage + ln.to[0][cb & 1] + off));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4 *)(stage + ln.to[1][cb & 1] + off));
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], st.o[cb], 0, 0, 0);
+        }
+    }
+}
+
+template <bool kDirect, bool kFp8>
+__global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
+{
+    using Lay = H128Layout<kFp8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kTotal];
+
+    int b, s, hg;
+    decode_work(p, b, s, hg);
+    int t_begin, t_end;
+    chunk_range(p, b, s, t_begin, t_end);
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = w >> 1;
+    Lane128 ln;
+    ln.c = w & 1;
+    ln.r16 = lane & 15;
+    ln.g4 = lane >> 4;
+    ln.r32 = lane & 31;
+    ln.g2 = lane >> 5;
+    const long long head0 = (long long)b * p.N + hg * 128;       // row of head 0
+    const long long qrow = head0 + 32 * g + 16 * ln.c + ln.r16;   // QK head
+    const long long orow = head0 + 32 * g + ln.r32;               // PV head
+
+    if (t_begin >= t_end) {
+        // empty split: (0, -inf), or out = 0 / lse = -inf when direct
+        const int hh = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 128;
+        if (kDirect) {
+            __bf16 *o = p.out + (head0 + hh) * kDV + c0;
+            for (int cc = 0; cc < 128; cc += 8)
+                *(bf16x8 *)(o + cc) = bf16x8{};
+            if (p.lse && (threadIdx.x & 3) == 0)
+                p.lse[head0 + hh] = -INFINITY;
+        } else {
+            float *o = p.part_out + ((head0 + hh) * p.S + s) * kDV + c0;
+            for (int cc = 0; cc < 128; cc += 4)
+                *(f32x4 *)(o + cc) = f32x4{};
+            if ((threadIdx.x & 3) == 0)
+                p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
+        }
+        return;
+    }
+
+    LDS_AS uint8_t *lds = AS3(smem);
+    LDS_AS uint8_t *pbuf = lds + Lay::kPbuf + g * (32 * 32 * 2);
+    LDS_AS float *abuf = (LDS_AS float *)(lds + Lay::kAbuf) + g * 32;
+
+    // QK A operand: row 16tb + r16, logical chunk 4k + g4
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        ln.ko[e] = ln.r16 * kRowBytes + ((4 * e) ^ ln.g4 ^ swz(ln.r16)) * 16;
+    // PV A operand (transposed reads): 16-lane group G reads token rows
+    // 16kk + 8*g2 + 4h + (j >> 2) and columns 256c + 32cb + 16(G & 1) + 4(j & 3)
+    {
+        const int G = lane >> 4, j = lane & 15;
+        const int cl = 2 * (G & 1) + ((j >> 1) & 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rr = 4 * h + (j >> 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                ln.to[h][e] = (8 * ln.g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 +
+                              8 * (j & 1) + 512 * ln.c;
+        }
+    }
+
+    float scale_log2 = p.scale_log2;
+    float out_scale = 1.0f;
+    if (kFp8) {
+        const float ks = *p.cache_scale;
+        scale_log2 *= ks;
+        out_scale = ks;
+    }
+
+    // query fragments (B operand of QK): head qrow, columns 32k + 8*g4 .. +8.
+    // Completed before any tile load is issued, so every later vmcnt wait
+    // counts tile loads only.
+    bf16x8 qf[18];
+    {
+        const __bf16 *qp = p.q + qrow * kD + ln.g4 * 8;
+#pragma unroll
+        for (int k = 0; k < 18; ++k)
+            qf[k] = *(const bf16x8 *)(qp + 32 * k);
+    }
+    wait_vmcnt<0>();
+
+    State128 st;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+        st.o[cb] = f32x16{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    const int ntiles = (t_end - t_begin + kT32 - 1) / kT32;
+    if (!kFp8) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            if (t < ntiles)
+                issue_tile32(p, lds + t * kStage32, w, lane, b, t_begin + t * kT32, t_end);
+        for (int t = 0; t < ntiles; ++t) {
+            // Wait for this wave's loads of tile t (t+1, t+2 may stay in
+            // flight); the barrier then makes every wave's loads visible and
+            // guarantees stage (t+3)%4 = (t-1)%4 and the probability buffer
+            // are no longer read.
+            const int after = ntiles - 1 - t;
+            wait_tiles128<false>(w, after < 2 ? after : 2);
+            barrier_no_fence();
+            if (t + 3 < ntiles)
+                issue_tile32(p, lds + ((t + 3) & 3) * kStage32, w, lane, b,
+                             t_begin + (t + 3) * kT32, t_end);
+            tile128(st, qf, lds + (t & 3) * kStage32, pbuf, abuf, ln, scale_log2,
+                    t_begin + t * kT32, t_end);
+        }
+    } else {
+        LDS_AS uint8_t *stg = lds + Lay::kStaging;
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            if (t < ntiles)
+                issue_tile32_fp8(p, stg + t * kStage8, w, lane, b, t_begin + t * kT32, t_end);
+        wait_tiles128<true>(w, ntiles - 1 < 2 ? ntiles - 1 : 2);
+        barrier_no_fence();
+        convert_tile32(stg, lds, tid);
+        barrier_no_fence();
+        if (3 < ntiles)
+            issue_tile32_fp8(p, stg, w, lane, b, t_begin + 3 * kT32, t_end);
+        for (int t = 0; t < ntiles; ++t) {
+            if (t + 1 < ntiles) {
+                // fp8 tile t+1 -> bf16 stage (t+1)%2; tiles t+2, t+3 may stay
+                // in flight.  The first barrier also retires tile t-1's use of
+                // that stage; the second retires the staging buffer, which is
+                // refilled with tile t+4.
+                const int after = ntiles - 2 - t;
+                wait_tiles128<true>(w, after < 2 ? after : 2);
+                barrier_no_fence();
+                convert_tile32(stg + ((t + 1) % 3) * kStage8, lds + ((t + 1) & 1) * kStage32, tid);
+                barrier_no_fence();
+                if (t + 4 < ntiles)
+                    issue_tile32_fp8(p, stg + ((t + 1) % 3) * kStage8, w, lane, b,
+                                     t_begin + (t + 4) * kT32, t_end);
+            }
+            tile128(st, qf, lds + (t & 1) * kStage32, pbuf, abuf, ln, scale_log2,
+                    t_begin + t * kT32, t_end);
+        }
+    }
+
+    // ---- epilogue: exchange (m, l) of the QK heads, normalise, write
+    float ltot = st.l + __shfl_xor(st.l, 16);
+    ltot += __shfl_xor(ltot, 32);
+    barrier_no_fence();   // every wave is done with pbuf / abuf
+    LDS_AS float *mbuf = (LDS_AS float *)(lds + Lay::kPbuf) + g * 64;
+    if (ln.g4 == 0) {
+        mbuf[16 * ln.c + ln.r16] = st.m;
+        mbuf[32 + 16 * ln.c + ln.r16] = ltot;
+    }
+    barrier_no_fence();
+    const float mh = mbuf[ln.r32];
+    const float lh = mbuf[32 + ln.r32];
+    const float inv = out_scale / lh;
+    const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
+    const int g2 = ln.g2;
+    if (kDirect) {
+        __bf16 *o = p.out + orow * kDV + 256 * ln.c;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int col = cb * 32 + q4 * 8 + g2 * 4;
+                const bf16x2 v0 = to_bf16x2(st.o[cb][4 * q4] * inv, st.o[cb][4 * q4 + 1] * inv);
+                const bf16x2 v1 = to_bf16x2(st.o[cb][4 * q4 + 2] * inv, st.o[cb][4 * q4 + 3] * inv);
+                *(bf16x4 *)(o + col) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
+            }
+        if (p.lse && ln.c == 0 && g2 == 0)
+            p.lse[orow] = lse_nat;
+    } else {
+        float *o = p.part_out + (orow * p.S + s) * kDV + 256 * ln.c;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int col = cb * 32 + q4 * 8 + g2 * 4;
+                *(f32x4 *)(o + col) = f32x4{st.o[cb][4 * q4] * inv, st.o[cb][4 * q4 + 1] * inv,
+                                            st.o[cb][4 * q4 + 2] * inv, st.o[cb][4 * q4 + 3] * inv};
+            }
+        if (ln.c == 0 && g2 == 0)
+            p.part_lse[orow * p.S + s] = lse_nat;
+    }
+}
+
+// ===========================================================================
+// 16 heads per workgroup: 4 waves, each with its own token stream (16-token
+// tiles; the WG's j-th tile goes to wave j % 4) and private LDS, merged
+// through LDS at the end.  QK^T on v_mfma_f32_16x16x32_bf16, PV on
+// v_mfma_f32_16x16x16_bf16.
+//   bf16 cache: 2 bf16 stages per wave (direct-to-LDS loads).
+//   fp8 cache: 2 fp8 staging buffers and 1 bf16 stage per wave; the wave
+//   widens each staged tile itself just before using it.
+// ===========================================================================
+constexpr int kT16 = 16;
+constexpr int kStage16 = kT16 * kRowBytes;                 // 18432 bytes
+constexpr int kStage16f8 = kT16 * kRowBytes8;              // 9216 bytes
+constexpr int kWaveLds16 = 2 * kStage16;                   // 36864 bytes per wave
+constexpr int kLoadsPerTile16 = kT16 * kRowChunks / 64;    // 18 DMA ops (bf16)
+constexpr int kLoadsPerTile16f8 = kT16 * kRowChunks8 / 64; // 9 DMA ops (fp8)
+
+__device__ __forceinline__ void issue_tile16(const Params &p, LDS_AS uint8_t *stage, int lane,
+                                             int b, int tile_start, int t_end)
+{
+    const int last = t_end - 1;
+    const int page = tile_start >> p.page_shift;   // 16-aligned tile: one page
+    const int blk = clamp_block(p.block_table[(long long)b * p.MB + page], p.num_blocks);
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base = p.cache + ((long long)blk << p.page_shift) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerTile16; ++j) {
+        const int q = j * 64 + lane;
+        const int r = q / kRowChunks;
+        int tok = tile_start + r;
+        tok = tok < last ? tok : last;
+        const int c = (q % kRowChunks) ^ swz(r);
+        dma16(base + (long long)(tok & pmask) * kRowBytes + c * 16, stage + j * 1024);
+    }
+}
+
+__device__ __forceinline__ void issue_tile16_fp8(const Params &p, LDS_AS uint8_t *stg, int lane,
+                                                 int b, int tile_start, int t_end)
+{
+    const int last = t_end - 1;
+    const int page = tile_start >> p.page_shift;
+    const int blk = clamp_block(p.block_table[(long long)b * p.MB + page], p.num_blocks);
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerTile16f8; ++j) {
+        const int q = j * 64 + lane;
+        const int r = q / kRowChunks8;
+        int tok = tile_start + r;
+        tok = tok < last ? tok : last;
+        dma16(base + (long long)(tok & pmask) * kRowBytes8 + (q % kRowChunks8) * 16,
+              stg + j * 1024);
+    }
+}
+
+// One wave widens its staged fp8 tile (16 rows) into its bf16 stage.
+__device__ __forceinline__ void convert_tile16(const LDS_AS uint8_t *stg, LDS_AS uint8_t *stage,
+                                               int lane)
+{
+#pragma unroll
+    for (int j = 0; j < kLoadsPerTile16f8; ++j) {
+        const int q = j * 64 + lane;
+        const int r = q / kRowChunks8, c = q % kRowChunks8;
+        const u32x4 v = *(const LDS_AS u32x4 *)(stg + r * kRowBytes8 + c * 16);
+        const u32x2 b0 = e4m3x4_to_bf16x4(v[0]), b1 = e4m3x4_to_bf16x4(v[1]);
+        const u32x2 b2 = e4m3x4_to_bf16x4(v[2]), b3 = e4m3x4_to_bf16x4(v[3]);
+        *(LDS_AS u32x4 *)(stage + r * kRowBytes + ((2 * c) ^ swz(r)) * 16) =
+            u32x4{b0[0], b0[1], b1[0], b1[1]};
+        *(LDS_AS u32x4 *)(stage + r * kRowBytes + ((2 * c + 1) ^ swz(r)) * 16) =
+            u32x4{b2[0], b2[1], b3[0], b3[1]};
+    }
+}
+
+struct State16 {
+    f32x4 o[32];      // O^T accumulators: 32 blocks of 16 output columns
+    float m;          // running max (log2), same in the 4 lanes of a head
+    float l;          // this lane's share of the row sum
+};
+
+__device__ __forceinline__ void compute_tile16(float scale_log2, State16 &st,
+                                               const bf16x8 (&qf)[18],
+                                               const LDS_AS uint8_t *stage,
+                                               const int (&ko)[2], const int (&vo)[4],
+                                               int lane, int tile_start, int t_end)
+{
+    f32x4 s0 = {}, s1 = {};
+#pragma unroll
+    for (int k = 0; k < 18; k += 2) {
+        const bf16x8 a0 = *(const LDS_AS bf16x8 *)(stage + ko[0] + (k >> 1) * 128);
+        const bf16x8 a1 = *(const LDS_AS bf16x8 *)(stage + ko[1] + (k >> 1) * 128);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[k], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k + 1], s1, 0, 0, 0);
+    }
+    const int g4 = lane >> 4;
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tile_start + g4 * 4 + i;
+        const float v = (s0[i] + s1[i]) * scale_log2;
+        x[i] = tok < t_end ? v : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+    }
+    if (wave_any(mx > st.m + kLazyRescale)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+        st.m = mnew;
+        st.l *= alpha;
+#pragma unroll
+        for (int c = 0; c < 32; ++c)
+            st.o[c] *= alpha;
+    }
+    const bf16x2 p01 = to_bf16x2(__builtin_amdgcn_exp2f(x[0] - st.m),
+                                 __builtin_amdgcn_exp2f(x[1] - st.m));
+    const bf16x2 p23 = to_bf16x2(__builtin_amdgcn_exp2f(x[2] - st.m),
+                                 __builtin_amdgcn_exp2f(x[3] - st.m));
+    st.l += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+    const bf16x4 pb = {p01[0], p01[1], p23[0], p23[1]};
+    const i16x4 pf = __builtin_bit_cast(i16x4, pb);
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+        const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(stage + vo[cb & 3] + (cb >> 2) * 128));
+        st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), pf,
+                                                             st.o[cb], 0, 0, 0);
+    }
+}
+
+template <bool kDirect, bool kFp8>
+__global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveLds16];
+
+    int b, s, hg;
+    decode_work(p, b, s, hg);
+    int t_begin, t_end;
+    chunk_range(p, b, s, t_begin, t_end);
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15;
+    const int g4 = lane >> 4;
+    const long long row_b0 = (long long)b * p.N + hg * 16;   // first head's row
+
+    if (t_begin >= t_end) {
+        // empty split: 16 heads x 512 columns, 256 threads
+        const int hh = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * 32;
+        if (kDirect) {
+            __bf16 *o = p.out + (row_b0 + hh) * kDV + c0;
+            for (int c = 0; c < 32; c += 8)
+                *(bf16x8 *)(o + c) = bf16x8{};
+            if (p.lse && (threadIdx.x & 15) == 0)
+                p.lse[row_b0 + hh] = -INFINITY;
+        } else {
+            float *o = p.part_out + ((row_b0 + hh) * p.S + s) * kDV + c0;
+            for (int c = 0; c < 32; c += 4)
+                *(f32x4 *)(o + c) = f32x4{};
+            if ((threadIdx.x & 15) == 0)
+                p.part_lse[(row_b0 + hh) * p.S + s] = -INFINITY;
+        }
+        return;
+    }
+
+    // QK A operand: row r16, logical chunk 4k + g4 (even / odd k)
+    int ko[2];
+    {
+        const int f = swz(r16);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ f) * 16;
+    }
+    // PV transposed reads: group g4 reads token rows 4*g4 .. +3, 16 columns
+    int vo[4];
+    {
+        const int j = lane & 15;
+        const int rr = 4 * g4 + (j >> 2);
+        const int cl = (j >> 1) & 1;
+        const int f = swz(rr);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            vo[m] = rr * kRowBytes + (((2 * m) ^ cl ^ f)) * 16 + 8 * (j & 1);
+    }
+
+    float scale_log2 = p.scale_log2;
+    float out_scale = 1.0f;
+    if (kFp8) {
+        const float ks = *p.cache_scale;
+        scale_log2 *= ks;
+        out_scale = ks;
+    }
+
+    // query fragments, completed before any tile load is issued so that the
+    // explicit vmcnt waits below only ever count tile loads
+    bf16x8 qf[18];
+    {
+        const __bf16 *qrow = p.q + (row_b0 + r16) * kD + g4 * 8;
+#pragma unroll
+        for (int k = 0; k < 18; ++k)
+            qf[k] = *(const bf16x8 *)(qrow + 32 * k);
+    }
+    wait_vmcnt<0>();
+
+    State16 st;
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+        st.o[c] = f32x4{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    LDS_AS uint8_t *mine_lds = AS3(smem) + w * kWaveLds16;
+    const int n16 = (t_end - t_begin + kT16 - 1) / kT16;
+    const int mine = n16 > w ? (n16 - w + 3) / 4 : 0;  // tiles w, w+4, ...
+    if (!kFp8) {
+        LDS_AS uint8_t *sa = mine_lds, *sb = mine_lds + kStage16;
+        if (mine > 0)
+            issue_tile16(p, sa, lane, b, t_begin + w * kT16, t_end);
+        for (int i = 0; i < mine; i += 2) {
+            const int tA = t_begin + (w + 4 * i) * kT16;
+            if (i + 1 < mine) {
+                issue_tile16(p, sb, lane, b, tA + 4 * kT16, t_end);
+                wait_vmcnt<kLoadsPerTile16>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            compute_tile16(scale_log2, st, qf, sa, ko, vo, lane, tA, t_end);
+            if (i + 1 >= mine)
+                break;
+            if (i + 2 < mine) {
+                issue_tile16(p, sa, lane, b, tA + 8 * kT16, t_end);
+                wait_vmcnt<kLoadsPerTile16>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            compute_tile16(scale_log2, st, qf, sb, ko, vo, lane, tA + 4 * kT16, t_end);
+        }
+    } else {
+        LDS_AS uint8_t *bst = mine_lds;
+        LDS_AS uint8_t *stg[2] = {mine_lds + kStage16, mine_lds + kStage16 + kStage16f8};
+        if (mine > 0)
+            issue_tile16_fp8(p, stg[0], lane, b, t_begin + w * kT16, t_end);
+        if (mine > 1)
+            issue_tile16_fp8(p, stg[1], lane, b, t_begin + (w + 4) * kT16, t_end);
+        for (int i = 0; i < mine; ++i) {
+            if (i + 1 < mine)
+                wait_vmcnt<kLoadsPerTile16f8>();
+            else
+                wait_vmcnt<0>();
+            convert_tile16(stg[i & 1], bst, lane);
+            if (i + 2 < mine)
+                issue_tile16_fp8(p, stg[i & 1], lane, b, t_begin + (w + 4 * (i + 2)) * kT16,
+                                 t_end);
+            compute_tile16(scale_log2, st, qf, bst, ko, vo, lane,
+                           t_begin + (w + 4 * i) * kT16, t_end);
+        }
+    }
+
+    // ---- merge the four waves' states through LDS, in two rounds of 256
+    // columns: [4 waves][16 heads][256] floats = 64 KiB, then (m, l).
+    float ltot = st.l + __shfl_xor(st.l, 16);
+    ltot += __shfl_xor(ltot, 32);
+    float *mo = (float *)smem;
+    float *ml = (float *)(smem + 65536);          // [4][16 heads][2]: m, l
+    const int hh = threadIdx.x >> 4;             // merge: head of this thread
+    const int c0 = (threadIdx.x & 15) * 16;      //        16 of the 256 columns
+    const long long row = row_b0 + hh;
+    float a[4], inv = 0.f, lse_nat = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        __syncthreads();
+#pragma unroll
+        for (int cb = 16 * rr; cb < 16 * rr + 16; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mo[(w * 16 + r16) * 256 + (cb - 16 * rr) * 16 + g4 * 4 + i] = st.o[cb][i];
+        if (rr == 0 && g4 == 0) {
+            ml[(w * 16 + r16) * 2 + 0] = st.m;
+            ml[(w * 16 + r16) * 2 + 1] = ltot;
+        }
+        __syncthreads();
+        if (rr == 0) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                M = fmaxf(M, ml[(v * 16 + hh) * 2]);
+            float Lsum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float mv = ml[(v * 16 + hh) * 2];
+                a[v] = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                Lsum += a[v] * ml[(v * 16 + hh) * 2 + 1];
+            }
+            inv = out_scale / Lsum;
+            lse_nat = (M + __builtin_amdgcn_logf(Lsum)) * kLn2;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; c += 4) {
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float acc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc += a[v] * mo[(v * 16 + hh) * 256 + c0 + c + e];
+                r[e] = acc * inv;
+            }
+            const int col = 256 * rr + c0 + c;
+            if (kDirect) {
+                const bf16x2 v0 = to_bf16x2(r[0], r[1]);
+                const bf16x2 v1 = to_bf16x2(r[2], r[3]);
+                *(bf16x4 *)(p.out + row * kDV + col) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
+            } else {
+                *(f32x4 *)(p.part_out + (row * p.S + s) * kDV + col) =
+                    f32x4{r[0], r[1], r[2], r[3]};
+            }
+        }
+    }
+    if ((threadIdx.x & 15) == 0) {
+        if (kDirect) {
+            if (p.lse)
+                p.lse[row] = lse_nat;
+        } else {
+            p.part_lse[row * p.S + s] = lse_nat;
+        }
+    }
+}
+
+// ===========================================================================
+// LSE merge: one wave per row, each lane owns 8 of the 512 columns.
+// ===========================================================================
+__global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_out,
+                                                 const float *__restrict__ part_lse,
+                                                 __bf16 *__restrict__ out,
+                                                 float *__restrict__ lse, int rows, int S)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int lane = threadIdx.x & 63;
+    const float *ls = part_lse + (long long)row * S;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s)
+        M = fmaxf(M, ls[s]);
+    __bf16 *o = out + (long long)row * kDV + lane * 8;
+    if (M == -INFINITY) {
+        *(bf16x8 *)o = bf16x8{};
+        if (lse && lane == 0)
+            lse[row] = -INFINITY;
+        return;
+    }
+    float Z = 0.f;
+    for (int s = 0; s < S; ++s)
+        Z += __builtin_amdgcn_exp2f((ls[s] - M) * kLog2e);
+    const float total = M + __builtin_amdgcn_logf(Z) * kLn2;
+    f32x4 acc0 = {}, acc1 = {};
+    const float *po = part_out + (long long)row * S * kDV + lane * 8;
+    for (int s = 0; s < S; ++s) {
+        const float wgt = __builtin_amdgcn_exp2f((ls[s] - total) * kLog2e);
+        const f32x4 v0 = *(const f32x4 *)(po + (long long)s * kDV);
+        const f32x4 v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
+        acc0 += wgt * v0;
+        acc1 += wgt * v1;
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (__bf16)acc0[e];
+        r[4 + e] = (__bf16)acc1[e];
+    }
+    *(bf16x8 *)o = r;
+    if (lse && lane == 0)
+        lse[row] = total;
+}
+
+// ===========================================================================
+// host side
+// ===========================================================================
+bool valid_shape(const mla_decode_shape_t *s, mla_status_t *err)
+{
+    if (s->batch < 0 || s->num_heads <= 0 || s->num_blocks <= 0 || s->page_size <= 0 ||
+        s->max_blocks_per_seq <= 0) {
+        *err = MLA_ERR_BAD_SHAPE;
+        return false;
+    }
+    if (s->kv_lora_rank != MLA_KV_LORA_RANK || s->qk_rope_head_dim != MLA_QK_ROPE_HEAD_DIM ||
+        s->num_heads % 16 != 0) {
+        *err = MLA_ERR_UNSUPPORTED;
+        return false;
+    }
+    if (s->page_size < 16 || s->page_size > 1024 || (s->page_size & (s->page_size - 1))) {
+        *err = MLA_ERR_UNSUPPORTED;
+        return false;
+    }
+    if (s->cache_dtype != MLA_CACHE_BF16 && s->cache_dtype != MLA_CACHE_FP8_E4M3FN) {
+        *err = MLA_ERR_UNSUPPORTED;
+        return false;
+    }
+    // grid = B * S * head groups must fit a 1-D launch
+    return true;
+}
+
+int log2_int(int v)
+{
+    int r = 0;
+    while ((1 << r) < v)
+        ++r;
+    return r;
+}
+
+mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void *cache,
+                          const float *cache_scale, const int32_t *block_table,
+                          const int32_t *seq_lens, float softmax_scale, int S,
+                          float *part_out, float *part_lse, void *out, float *lse,
+                          hipStream_t stream)
+{
+    Params p;
+    p.q = (const __bf16 *)q;
+    p.cache = (const uint8_t *)cache;
+    p.cache_scale = cache_scale;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.part_out = part_out;
+    p.part_lse = part_lse;
+    p.out = (__bf16 *)out;
+    p.lse = lse;
+    p.scale_log2 = softmax_scale * kLog2e;
+    p.B = s->batch;
+    p.N = s->num_heads;
+    p.S = S;
+    p.MB = s->max_blocks_per_seq;
+    p.num_blocks = s->num_blocks;
+    p.page_shift = log2_int(s->page_size);
+    const bool direct = part_out == nullptr;
+    const bool wide = s->num_heads % 128 == 0;
+    p.HG = wide ? s->num_heads / 128 : s->num_heads / 16;
+    const long long grid = (long long)s->batch * S * p.HG;
+    if (grid > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    dim3 g((unsigned)grid), blk(wide ? 512 : 256);
+    const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
+#define MLA_LAUNCH(KERNEL)                                                              \
+    do {                                                                                \
+        if (direct && fp8) hipLaunchKernelGGL((KERNEL<true, true>), g, blk, 0, stream, p);    \
+        else if (direct) hipLaunchKernelGGL((KERNEL<true, false>), g, blk, 0, stream, p);     \
+        else if (fp8) hipLaunchKernelGGL((KERNEL<false, true>), g, blk, 0, stream, p);        \
+        else hipLaunchKernelGGL((KERNEL<false, false>), g, blk, 0, stream, p);                \
+    } while (0)
+    if (wide)
+        MLA_LAUNCH(mla_split_h128);
+    else
+        MLA_LAUNCH(mla_split_h16);
+#undef MLA_LAUNCH
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t launch_merge(int rows, int S, const float *part_out, const float *part_lse,
+                          void *out, float *lse, hipStream_t stream)
+{
+    if (rows == 0)
+        return MLA_OK;
+    dim3 g((unsigned)((rows + 3) / 4)), blk(256);
+    hipLaunchKernelGGL(mla_merge, g, blk, 0, stream, part_out, part_lse, (__bf16 *)out, lse,
+                       rows, S);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t partial_bytes(const mla_decode_shape_t *s, int S)
+{
+    return (size_t)s->batch * (size_t)s->num_heads * (size_t)S * (kDV + 1) * sizeof(float);
+}
+
+mla_status_t check_common(const mla_decode_shape_t *shape, const void *q, const void *cache,
+                          const float *cache_scale, const int32_t *block_table,
+                          const int32_t *seq_lens, int32_t S)
+{
+    if (!shape)
+        return MLA_ERR_NULL_POINTER;
+    mla_status_t err = MLA_OK;
+    if (!valid_shape(shape, &err))
+        return err;
+    if (S < 1 || S > MLA_MAX_KV_SPLITS)
+        return MLA_ERR_BAD_SPLITS;
+    if (shape->batch > 0 && (!q || !cache || !block_table || !seq_lens))
+        return MLA_ERR_NULL_POINTER;
+    if (shape->cache_dtype == MLA_CACHE_FP8_E4M3FN ? cache_scale == nullptr
+                                                    : cache_scale != nullptr)
+        return cache_scale ? MLA_ERR_UNSUPPORTED : MLA_ERR_NULL_POINTER;
+    return MLA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *mla_status_string(mla_status_t status)
+{
+    switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER: a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: a dimension is negative or inconsistent";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not handled by this build";
+    case MLA_ERR_BAD_SPLITS: return "MLA_ERR_BAD_SPLITS: num_kv_splits outside [1, 256]";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime rejected a launch";
+    }
+    return "unknown mla_status_t";
+}
+
+size_t mla_decode_workspace_size(const mla_decode_shape_t *shape, int32_t num_kv_splits)
+{
+    if (!shape || num_kv_splits < 1 || num_kv_splits > MLA_MAX_KV_SPLITS || shape->batch < 0 ||
+        shape->num_heads < 0)
+        return 0;
+    if (num_kv_splits == 1)
+        return 0;
+    return partial_bytes(shape, num_kv_splits);
+}
+
+mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q, const void *latent_cache,
+                        const float *cache_scale, const int32_t *block_table,
+                        const int32_t *seq_lens, float softmax_scale, int32_t num_kv_splits,
+                        void *workspace, size_t workspace_bytes, void *out, float *lse,
+                        hipStream_t stream)
+{
+    mla_status_t err = check_common(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                                    num_kv_splits);
+    if (err != MLA_OK)
+        return err;
+    if (shape->batch > 0 && !out)
+        return MLA_ERR_NULL_POINTER;
+    const size_t need = mla_decode_workspace_size(shape, num_kv_splits);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MLA_ERR_WORKSPACE;
+    if (shape->batch == 0)
+        return MLA_OK;
+    if (num_kv_splits == 1)
+        return launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                            softmax_scale, 1, nullptr, nullptr, out, lse, stream);
+    float *part_out = (float *)workspace;
+    float *part_lse = part_out + (size_t)shape->batch * shape->num_heads * num_kv_splits * kDV;
+    err = launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens, softmax_scale,
+                       num_kv_splits, part_out, part_lse, nullptr, nullptr, stream);
+    if (err != MLA_OK)
+        return err;
+    return launch_merge(shape->batch * shape->num_heads, num_kv_splits, part_out, part_lse, out,
+                        lse, stream);
+}
+
+mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
+                                 const void *latent_cache, const float *cache_scale,
+                                 const int32_t *block_table, const int32_t *seq_lens,
+                                 float softmax_scale, int32_t num_kv_splits, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
+{
+    mla_status_t err = check_common(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                                    num_kv_splits);
+    if (err != MLA_OK)
+        return err;
+    const size_t need = partial_bytes(shape, num_kv_splits);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MLA_ERR_WORKSPACE;
+    if (shape->batch == 0)
+        return MLA_OK;
+    float *part_out = (float *)workspace;
+    float *part_lse = part_out + (size_t)shape->batch * shape->num_heads * num_kv_splits * kDV;
+    return launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens, softmax_scale,
+                        num_kv_splits, part_out, part_lse, nullptr, nullptr, stream);
+}
+
+mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *part_out,
+                              const float *part_lse, void *out, float *lse, hipStream_t stream)
+{
+    if (rows < 0)
+        return MLA_ERR_BAD_SHAPE;
+    if (S < 1 || S > MLA_MAX_KV_SPLITS)
+        return MLA_ERR_BAD_SPLITS;
+    if (dv != kDV)
+        return MLA_ERR_UNSUPPORTED;
+    if (rows > 0 && (!part_out || !part_lse || !out))
+        return MLA_ERR_NULL_POINTER;
+    return launch_merge(rows, S, part_out, part_lse, out, lse, stream);
+}
+
+} // extern "C"

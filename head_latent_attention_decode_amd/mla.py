@@ -1,0 +1,216 @@
+"""Python binding of the C ABI in include/mla_decode.h (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module only turns
+torch tensors into pointers and sizes, supplies the current HIP stream, and
+raises when the library returns a non-OK status.  PyTorch provides device
+memory and streams, nothing else.  There is no fallback: if the library is
+missing, every call raises.
+
+The operation is the decode of the data-movement-friendly MLA path (vLLM API
+docs, vllm.model_executor.layers.attention.mla_attention, module docstring,
+"Data-Movement Friendly Approach (i.e. forward_mqa)") with the functional
+signature of mla_attention_decode (Model-Optimizer docs,
+modelopt.torch.kernels.quantization.attention.mla): see include/mla_decode.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmla_decode.so"
+_lib = None
+
+MLA_OK = 0
+MLA_CACHE_BF16 = 0
+MLA_CACHE_FP8_E4M3FN = 1
+KV_LORA_RANK = 512
+QK_ROPE_HEAD_DIM = 64
+HEAD_SIZE = KV_LORA_RANK + QK_ROPE_HEAD_DIM
+MAX_KV_SPLITS = 256
+
+EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
+            "mla_decode_partials", "mla_merge_states")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("kv_lora_rank", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load(path: Path | str | None = None):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else _LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is missing: build it with head_latent_attention_decode_amd."
+                           "build.build_library() (or __graft_entry__.build())")
+    lib = ctypes.CDLL(str(p))
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeShape), i32]
+    lib.mla_decode.restype = ctypes.c_int
+    lib.mla_decode.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
+                               ctypes.c_float, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_partials.restype = ctypes.c_int
+    lib.mla_decode_partials.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
+                                        ctypes.c_float, i32, vp, sz, vp]
+    lib.mla_merge_states.restype = ctypes.c_int
+    lib.mla_merge_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _cache_dtype(latent_cache: torch.Tensor, cache_dtype):
+    if cache_dtype is not None:
+        if cache_dtype in ("bf16", MLA_CACHE_BF16, torch.bfloat16):
+            return MLA_CACHE_BF16
+        if cache_dtype in ("fp8_e4m3fn", MLA_CACHE_FP8_E4M3FN, torch.float8_e4m3fn):
+            return MLA_CACHE_FP8_E4M3FN
+        raise ValueError(f"unknown cache dtype {cache_dtype!r}")
+    if latent_cache.dtype == torch.bfloat16:
+        return MLA_CACHE_BF16
+    if latent_cache.dtype == torch.float8_e4m3fn:
+        return MLA_CACHE_FP8_E4M3FN
+    # raw bytes are ambiguous (E4M3 or a packed 4-bit format): make the caller say
+    raise ValueError("a uint8 cache needs an explicit cache_dtype")
+
+
+def make_shape(q, latent_cache, block_table, cache_dtype=None) -> DecodeShape:
+    if q.dim() != 3 or latent_cache.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("expected q [B, N, 576], latent_cache [blocks, page, 576], "
+                         "block_table [B, max_blocks]")
+    B, N, D = q.shape
+    nb, P, Dc = latent_cache.shape
+    if D != HEAD_SIZE or Dc != HEAD_SIZE:
+        raise ValueError("query and cache rows must be 576 wide (512 latent + 64 rope)")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows must equal the batch")
+    return DecodeShape(B, N, KV_LORA_RANK, QK_ROPE_HEAD_DIM, nb, P, block_table.shape[1],
+                       _cache_dtype(latent_cache, cache_dtype))
+
+
+def workspace_size(shape: DecodeShape, num_kv_splits: int) -> int:
+    return int(load().mla_decode_workspace_size(ctypes.byref(shape), int(num_kv_splits)))
+
+
+def _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale):
+    for name, t in (("q", q), ("latent_cache", latent_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if cache_scale is not None and (cache_scale.dtype != torch.float32 or not cache_scale.is_cuda
+                                    or cache_scale.numel() != 1):
+        raise ValueError("cache_scale must be a one-element float32 device tensor")
+
+
+def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
+               cache_scale=None, cache_dtype=None, out=None, lse=None, return_lse=True,
+               workspace=None):
+    """Decode attention: returns (out bf16 [B, N, 512], lse f32 [B, N] or None)."""
+    _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale)
+    shape = make_shape(q, latent_cache, block_table, cache_dtype)
+    B, N = shape.batch, shape.num_heads
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, N, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    need = workspace_size(shape, num_kv_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().mla_decode(ctypes.byref(shape), _ptr(q), _ptr(latent_cache), _ptr(cache_scale),
+                           _ptr(block_table), _ptr(seq_lens), float(softmax_scale),
+                           int(num_kv_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                           _stream(dev))
+    _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_partials(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
+                        cache_scale=None, cache_dtype=None, workspace=None):
+    """The split stage alone: returns (part_out f32 [B, N, S, 512], part_lse f32 [B, N, S])."""
+    _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale)
+    shape = make_shape(q, latent_cache, block_table, cache_dtype)
+    B, N, S = shape.batch, shape.num_heads, int(num_kv_splits)
+    count = B * N * S * (KV_LORA_RANK + 1)
+    if workspace is None:
+        workspace = torch.empty(count, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().mla_decode_partials(ctypes.byref(shape), _ptr(q), _ptr(latent_cache),
+                                    _ptr(cache_scale), _ptr(block_table), _ptr(seq_lens),
+                                    float(softmax_scale), S, _ptr(workspace), ws_bytes,
+                                    _stream(q.device))
+    _check(st, "mla_decode_partials")
+    flat = workspace.view(torch.float32)[:count]
+    part_out = flat[: B * N * S * KV_LORA_RANK].view(B, N, S, KV_LORA_RANK)
+    part_lse = flat[B * N * S * KV_LORA_RANK:].view(B, N, S)
+    return part_out, part_lse
+
+
+def mla_merge_states(part_out, part_lse, *, out=None, lse=None, return_lse=True):
+    """S-way LSE merge: part_out f32 [..., S, 512], part_lse f32 [..., S] -> (out bf16, lse f32)."""
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    *lead, S, dv = part_out.shape
+    if tuple(part_lse.shape) != (*lead, S):
+        raise ValueError("part_lse shape does not match part_out")
+    rows = 1
+    for d in lead:
+        rows *= d
+    if out is None:
+        out = torch.empty((*lead, dv), dtype=torch.bfloat16, device=part_out.device)
+    if return_lse and lse is None:
+        lse = torch.empty(tuple(lead), dtype=torch.float32, device=part_out.device)
+    if not return_lse:
+        lse = None
+    st = load().mla_merge_states(rows, S, dv, _ptr(part_out), _ptr(part_lse), _ptr(out),
+                                 _ptr(lse), _stream(part_out.device))
+    _check(st, "mla_merge_states")
+    return out, lse

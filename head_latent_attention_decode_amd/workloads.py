@@ -145,17 +145,19 @@ def _normal_rows(seed: int, n_rows: int, width: int, threads: int):
 def make_workload(B, N, page_size, seq_lens, *, seed, num_kv_splits=1,
                   cache_dtype="bf16", max_len=None, name="custom",
                   softmax_scale=DEFAULT_SOFTMAX_SCALE, head_size=HEAD_SIZE,
-                  threads=None, poison=True) -> Workload:
+                  threads=None, poison=True, perm_seed=None) -> Workload:
     """Build one seeded workload (see the module docstring for the recipe).
 
     max_len sets max_blocks_per_seq = ceil(max_len / page_size) (default: the
-    longest drawn length, at least one page).
+    longest drawn length, at least one page).  perm_seed (default seed + 7919)
+    seeds the page permutation alone, so two workloads that differ only in it
+    hold the same rows at different physical pages.
     """
     if cache_dtype not in ("bf16", "fp8_e4m3fn"):
         raise ValueError(cache_dtype)
     threads = threads or min(16, max(1, torch.get_num_threads()))
     lens = draw_seq_lens(seq_lens, B, seed)
-    rng = np.random.default_rng(seed + 7919)
+    rng = np.random.default_rng(seed + 7919 if perm_seed is None else perm_seed)
     pages = (lens.astype(np.int64) + page_size - 1) // page_size
     total_pages = int(pages.sum())
     if max_len is None:

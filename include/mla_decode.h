@@ -1,0 +1,190 @@
+/*
+ * mla_decode.h: C ABI of the MI355X (gfx950) MLA decode library.
+ *
+ * The operation: one absorbed query token per request attends over that
+ * request's rows of a paged latent KV cache.  A query is cat[ql_nope, q_pe]
+ * of width kv_lora_rank + qk_rope_head_dim = 512 + 64 = 576; a cache row is
+ * cat[kv_c, k_pe] of the same width; the value of a row is its kv_c part
+ * (its first 512 columns).  This is the data-movement-friendly path of
+ * multi-head latent attention:
+ *   - vLLM API docs, vllm.model_executor.layers.attention.mla_attention,
+ *     module docstring, "Data-Movement Friendly Approach (i.e. forward_mqa)":
+ *     SDPA(cat[ql_nope, q_pe], cat[kv_c, k_pe], kv_c), a multi-query
+ *     attention with QK width Lkv + R and value width Lkv.
+ *   - Model-Optimizer docs, modelopt.torch.kernels.quantization.attention.mla,
+ *     mla_attention_decode: arguments q, latent_cache, block_table,
+ *     b_seq_len, softmax_scale, num_kv_splits, return_lse; result
+ *     (out [batch, num_heads, 512], lse [batch, num_heads] | None).
+ *
+ * For request b with L = seq_lens[b] and head n:
+ *     s_t   = softmax_scale * <q[b,n,:], K_t>            t = 0 .. L-1
+ *     lse   = ln sum_t exp(s_t)
+ *     out_l = sum_t exp(s_t - lse) * K_t[l]                l = 0 .. 511
+ * where K_t is row (t mod page_size) of block block_table[b][t / page_size].
+ * L == 0 gives out = 0 and lse = -inf, the state that carries no weight in a
+ * merge (vLLM API docs, neutralize_empty_context_partials).
+ *
+ * Work is split over the KV axis into num_kv_splits contiguous chunks per
+ * request; each chunk yields a partial (normalised output, LSE) and the
+ * partials are combined with the LSE merge.  The split count is a fixed
+ * argument, so the reduction order depends only on (seq_len, num_kv_splits,
+ * num_heads), never on the batch or the device ("num_kv_splits: fixed split
+ * count ... kept fixed by default for reproducibility across batch shapes and
+ * devices", Model-Optimizer docs, mla_attention_decode, "Parameters").
+ * Chunk s of a request of length L covers tokens
+ *     [s*C, min((s+1)*C, L)),  C = 32 * ceil(ceil(L / num_kv_splits) / 32);
+ * trailing chunks may be empty.
+ *
+ * Memory and threading contract, for every entry point:
+ *   - Pointers marked "device" point to device memory allocated by the
+ *     caller; the library allocates nothing, keeps no pointer after it
+ *     returns, and holds no state: calls are reentrant.
+ *   - Every call only enqueues kernels on `stream` and returns.  It performs
+ *     no host<->device copy and never reads device data on the host, so the
+ *     launch configuration depends only on the shape arguments and the calls
+ *     can be captured into a HIP graph.
+ *   - Arguments the host can check are checked before anything is launched;
+ *     a failed check returns an error status and launches nothing.
+ *   - Device-side data is not validated on the host.  Preconditions the caller
+ *     owns: 0 <= seq_lens[b] <= max_blocks_per_seq * page_size, and the first
+ *     ceil(seq_lens[b] / page_size) entries of block_table row b are in
+ *     [0, num_blocks).  The kernels clamp both into range before addressing
+ *     memory, so a violation gives wrong numbers for that request, never an
+ *     out-of-bounds access.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+    MLA_ERR_BAD_SHAPE = 2,      /* a dimension is negative or inconsistent */
+    MLA_ERR_UNSUPPORTED = 3,    /* a shape or dtype this build does not handle */
+    MLA_ERR_BAD_SPLITS = 4,     /* num_kv_splits outside [1, MLA_MAX_KV_SPLITS] */
+    MLA_ERR_WORKSPACE = 5,      /* workspace missing or smaller than required */
+    MLA_ERR_HIP = 6             /* the HIP runtime rejected a launch */
+} mla_status_t;
+
+/* Cache element type.  It is explicit because the bytes alone are ambiguous:
+ * a uint8 cache must be read as E4M3, not as a packed 4-bit format, which
+ * would double the apparent row width (raon-1-mini mla_attention.py,
+ * _attn_read_kv_cache). */
+typedef enum {
+    MLA_CACHE_BF16 = 0,         /* bfloat16 rows, 1152 bytes each */
+    MLA_CACHE_FP8_E4M3FN = 1    /* OCP E4M3 ("FN": no inf, max 448) rows,
+                                   576 bytes each, times a per-tensor scale */
+} mla_cache_dtype_t;
+
+#define MLA_KV_LORA_RANK 512
+#define MLA_QK_ROPE_HEAD_DIM 64
+#define MLA_MAX_KV_SPLITS 256
+
+typedef struct {
+    int32_t batch;              /* B >= 0 requests, one query token each */
+    int32_t num_heads;          /* N > 0, a multiple of 16 */
+    int32_t kv_lora_rank;       /* must be 512 */
+    int32_t qk_rope_head_dim;   /* must be 64 */
+    int32_t num_blocks;         /* physical pages in the cache, > 0 */
+    int32_t page_size;          /* rows per page: 16, 32, 64 or 128 */
+    int32_t max_blocks_per_seq; /* columns of block_table, > 0 */
+    mla_cache_dtype_t cache_dtype;
+} mla_decode_shape_t;
+
+/* Human-readable name of a status; never NULL. */
+const char *mla_status_string(mla_status_t status);
+
+/* Bytes of device workspace mla_decode needs for this shape and split
+ * count: B * N * S * (512 + 1) * 4 (fp32 partial outputs and LSEs), or 0
+ * when num_kv_splits == 1 (the single chunk is written to `out` directly).
+ * Returns 0 for a NULL shape or an invalid split count. */
+size_t mla_decode_workspace_size(const mla_decode_shape_t *shape,
+                                 int32_t num_kv_splits);
+
+/*
+ * Decode attention, split over KV and merged.
+ *
+ *   q             device, bf16 [B, N, 576], contiguous: cat[ql_nope, q_pe].
+ *   latent_cache  device, [num_blocks, page_size, 576] contiguous rows
+ *                 cat[kv_c, k_pe]; bf16, or E4M3 bytes per cache_dtype.
+ *   cache_scale   device, one float: the per-tensor dequantisation scale of
+ *                 an fp8 cache (the cache stores latent / scale; readers
+ *                 multiply it back into both kv_c and k_pe, raon-1-mini
+ *                 mla_attention.py, dequantize_context_latent).  Must be
+ *                 NULL for a bf16 cache, non-NULL for fp8.
+ *   block_table   device, int32 [B, max_blocks_per_seq]: logical page i of
+ *                 request b lives in physical block block_table[b][i].
+ *   seq_lens      device, int32 [B]: KV length of each request, the current
+ *                 token included.  0 is allowed (padding rows).
+ *   softmax_scale the scale applied to the full 576-wide dot product
+ *                 (required; an MLA layer folds its mscale into it).
+ *   num_kv_splits S in [1, 256], fixed by the caller.
+ *   workspace     device, at least mla_decode_workspace_size() bytes; may
+ *                 be NULL when that size is 0.  Overwritten.
+ *   out           device, bf16 [B, N, 512], written in full (the pages' default
+ *                 output dtype is the model compute dtype, which is bf16 for
+ *                 both cache types).  Rounded to nearest even.
+ *   lse           device, float [B, N] natural-log LSE, or NULL to skip it.
+ *   stream        HIP stream the kernels are enqueued on (0 = null stream).
+ *
+ * Returns MLA_OK after enqueuing, or an error status with nothing enqueued
+ * (MLA_ERR_HIP if a launch itself failed).  B == 0 is a no-op.
+ */
+mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q,
+                        const void *latent_cache, const float *cache_scale,
+                        const int32_t *block_table, const int32_t *seq_lens,
+                        float softmax_scale, int32_t num_kv_splits,
+                        void *workspace, size_t workspace_bytes, void *out,
+                        float *lse, hipStream_t stream);
+
+/*
+ * The split stage of mla_decode alone: writes the per-chunk partial states
+ *   part_out  = workspace as float [B, N, S, 512] (normalised chunk outputs)
+ *   part_lse  = workspace + B*N*S*512 floats, float [B, N, S] (natural log)
+ * with (0, -inf) for an empty chunk.  Same arguments and checks as
+ * mla_decode; requires num_kv_splits >= 1 and a workspace of
+ * B * N * S * 513 * 4 bytes (for S == 1 too).  mla_decode is exactly this
+ * followed by mla_merge_states on the same workspace.
+ */
+mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
+                                 const void *latent_cache,
+                                 const float *cache_scale,
+                                 const int32_t *block_table,
+                                 const int32_t *seq_lens, float softmax_scale,
+                                 int32_t num_kv_splits, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * S-way LSE merge of partial attention states (the combination performed by
+ * merge_attn_states for two states in the vLLM API docs, "Chunked Prefill",
+ * here for S states with the decode layout):
+ *     lse[r]    = ln sum_s exp(part_lse[r, s])
+ *     out[r, l] = sum_s exp(part_lse[r, s] - lse[r]) * part_out[r, s, l]
+ * A state with lse = -inf carries no weight; a row whose states are all
+ * -inf gives out = 0 and lse = -inf.
+ *
+ *   rows      number of rows R = B * N (>= 0).
+ *   S         states per row, in [1, 256].
+ *   dv        row width; must be 512.
+ *   part_out  device, float [R, S, dv].
+ *   part_lse  device, float [R, S].
+ *   out       device, bf16 [R, dv] (round to nearest even).
+ *   lse       device, float [R], or NULL.
+ */
+mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
+                              const float *part_out, const float *part_lse,
+                              void *out, float *lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,200 @@
+"""Parity of the HIP decode path with the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI (libmla_decode.so) via the ctypes binding.
+Small cases are compared in full; the five named workloads at full size are
+compared on sampled (b, n) rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_latent_attention_decode_amd import mla
+from head_latent_attention_decode_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+LENS = [1, 17, 31, 32, 33, 100, 129, 1000]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_workload():
+    wl = W.config_workload("tiny")
+    out, lse = G.run(wl)
+    ref_o, ref_l = G.reference(wl)
+    e = G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what="tiny")
+    _say("tiny", e)
+
+
+@pytest.mark.parametrize("N", [16, 32, 48, 128, 256])
+@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_small_grid(N, page, S):
+    wl = W.make_workload(len(LENS), N, page, LENS, seed=100 + N + page + S)
+    _say("case", N, page, S)
+    out, lse = G.run(wl, S)
+    ref_o, ref_l = G.reference(wl)
+    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what=f"N={N} P={page} S={S}")
+
+
+@pytest.mark.parametrize("N", [16, 128])
+@pytest.mark.parametrize("S", [1, 2, 5])
+def test_fp8_small(N, S):
+    lens = [1, 40, 64, 65, 300, 777]
+    wl = W.make_workload(len(lens), N, 64, lens, seed=200 + N + S, cache_dtype="fp8_e4m3fn")
+    _say("fp8 case", N, S)
+    out, lse = G.run(wl, S)
+    ref_o, ref_l = G.reference(wl)
+    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn", what=f"fp8 N={N} S={S}")
+
+
+@pytest.mark.parametrize("N", [16, 128])
+@pytest.mark.parametrize("S", [1, 4])
+def test_zero_length_rows(N, S):
+    lens = [0, 5, 0, 70]
+    wl = W.make_workload(4, N, 16, lens, seed=300 + N, max_len=128)
+    out, lse = G.run(wl, S)
+    ref_o, ref_l = G.reference(wl)
+    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what=f"zero rows N={N} S={S}")
+
+
+def test_all_rows_empty():
+    wl = W.make_workload(3, 128, 64, [0, 0, 0], seed=7, max_len=64)
+    for S in (1, 2):
+        out, lse = G.run(wl, S)
+        assert (out == 0).all() and torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_split_count_invariance(N):
+    lens = [2049, 517, 64]
+    wl = W.make_workload(3, N, 64, lens, seed=400 + N)
+    ref_o, ref_l = G.reference(wl)
+    outs = {}
+    for S in (1, 2, 3, 4, 7, 8, 32, 64):
+        out, lse = G.run(wl, S)
+        G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what=f"S={S}")
+        outs[S] = (out, lse)
+    # all split counts agree with each other to the same tolerance
+    for S, (o, l) in outs.items():
+        d = (o - outs[1][0]).abs().amax(-1) / outs[1][0].abs().amax(-1)
+        assert float(d.max()) <= 1e-2, S
+        assert float((l - outs[1][1]).abs().max()) <= 2e-3, S
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_page_permutation_bitwise(N):
+    lens = [300, 1, 129]
+    a = W.make_workload(3, N, 16, lens, seed=500, perm_seed=1)
+    b = W.make_workload(3, N, 16, lens, seed=500, perm_seed=2)
+    assert not torch.equal(a.block_table, b.block_table)
+    for S in (1, 3):
+        oa, la = G.run(a, S)
+        ob, lb = G.run(b, S)
+        assert torch.equal(oa, ob) and torch.equal(la, lb), "result depends on page placement"
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_run_to_run_bitwise(N):
+    wl = W.make_workload(4, N, 64, [100, 2000, 5, 999], seed=600 + N)
+    d = G.to_device(wl)
+    first = G.run(wl, 4, dev_inputs=d)
+    for _ in range(3):
+        again = G.run(wl, 4, dev_inputs=d)
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_batch_invariance(N):
+    """A request alone and the same request inside a batch give the same bits."""
+    lens = [700, 3000, 41]
+    big = W.make_workload(3, N, 64, lens, seed=700 + N)
+    ob, lb = G.run(big, 8)
+    for b in range(3):
+        L = int(lens[b])
+        pages = -(-L // 64)
+        one = W.Workload(name="one", q=big.q[b:b + 1].clone(), cache=big.cache,
+                         block_table=big.block_table[b:b + 1, :pages].clone().contiguous(),
+                         seq_lens=big.seq_lens[b:b + 1].clone(), softmax_scale=big.softmax_scale,
+                         cache_scale=big.cache_scale, cache_dtype=big.cache_dtype,
+                         num_kv_splits=8, seed=0)
+        o1, l1 = G.run(one, 8)
+        assert torch.equal(o1[0], ob[b]) and torch.equal(l1[0], lb[b]), f"request {b}"
+
+
+def test_no_lse_output():
+    wl = W.make_workload(2, 128, 64, [90, 10], seed=800)
+    out_a, _ = G.run(wl, 2)
+    out_b, lse_b = G.run(wl, 2, return_lse=False)
+    assert lse_b is None and torch.equal(out_a, out_b)
+
+
+@pytest.mark.parametrize("N,S", [(16, 3), (128, 5)])
+def test_partials_match_oracle_spans(N, S):
+    """The split stage alone against the oracle's attention over each chunk,
+    with chunk s = [s*C, min((s+1)*C, L)), C = 32*ceil(ceil(L/S)/32)."""
+    lens = [1, 70, 333, 64]
+    wl = W.make_workload(4, N, 16, lens, seed=900 + N)
+    d = G.to_device(wl)
+    po, pl = mla.mla_decode_partials(d["q"], d["latent_cache"], d["block_table"], d["seq_lens"],
+                                     wl.softmax_scale, S)
+    torch.cuda.synchronize()
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    rb, rn, t0, t1 = [], [], [], []
+    for b, L in enumerate(lens):
+        C = 32 * (-(-(-(-L // S)) // 32))
+        for n in range(N):
+            for s in range(S):
+                a = min(s * C, L)
+                e = min(s * C + C, L)
+                rb.append(b); rn.append(n); t0.append(a); t1.append(e)
+    ref_o, ref_l = oracle.attend_spans(G.problem(wl), rb, rn, t0, t1)
+    span = np.array(t1) - np.array(t0)
+    G.check(po.reshape(-1, 512), pl.reshape(-1), ref_o, ref_l, span, what="partials")
+
+
+def test_merge_kernel_against_oracle():
+    g = torch.Generator().manual_seed(11)
+    R, S = 300, 7
+    po = torch.randn(R, S, 512, generator=g)
+    pl = torch.randn(R, S, generator=g) * 3
+    pl[torch.rand(R, S, generator=g) < 0.3] = -float("inf")
+    pl[:5] = -float("inf")                       # rows with no weight at all
+    out, lse = mla.mla_merge_states(po.cuda(), pl.cuda())
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.merge_states(po.double().numpy(), pl.double().numpy())
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    assert (out[:5] == 0).all() and np.isneginf(lse[:5]).all()
+    live = np.isfinite(ref_l)
+    assert (np.isfinite(lse) == live).all()
+    err = np.abs(out[live] - ref_o[live]).max(axis=1) / np.abs(ref_o[live]).max(axis=1)
+    assert err.max() <= 8e-3, err.max()       # bf16 output rounding dominates
+    assert np.abs(lse[live] - ref_l[live]).max() <= 1e-5
+
+
+def _sample_rows(wl, n_rows, seed):
+    rng = np.random.default_rng(seed)
+    lens = wl.seq_lens.numpy()
+    bs = list(rng.integers(0, wl.B, n_rows - 4)) + [int(lens.argmax()), int(lens.argmin())] * 2
+    ns = list(rng.integers(0, wl.N, n_rows - 4)) + [0, wl.N - 1, wl.N - 1, 0]
+    return np.array(bs), np.array(ns)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "ragged", "long_context", "fp8_cache"])
+def test_full_size_workloads_sampled(name):
+    _say("generating", name)
+    wl = W.config_workload(name)
+    _say("running", name, "S =", wl.num_kv_splits)
+    out, lse = G.run(wl)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rb, rn = _sample_rows(wl, 48, seed=1)
+    _say("oracle on", len(rb), "sampled rows")
+    ref_o, ref_l = G.reference(wl, rows=(rb, rn))
+    lens = wl.seq_lens.numpy()[rb]
+    e = G.check(out[rb, rn], lse[rb, rn], ref_o, ref_l, lens, dtype=wl.cache_dtype, what=name)
+    _say(name, "max errors", e)
