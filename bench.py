@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA decode step on one MI355X.
+
+A step is one mla_decode call (split kernel + LSE-merge kernel) over one
+batch of the DeepSeek-V3-shaped decode workload: B = 64 requests, N = 128
+heads, 4096 cached tokens each, page size 64, bf16 query and cache,
+num_kv_splits = 4.  Inputs are synthetic (seeded), generated on the host and
+resident in HBM before the timed region; three copies of the query, cache
+and page table are rotated so that no step finds its KV rows in the 256 MB
+Infinity Cache left behind by the previous step.
+
+Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
+(GB/s: every KV row read once, plus q, out, lse, page-table entries and
+lengths), per-step time, TFLOP/s, the split kernel's roofline fraction
+(its duration measured with HIP events on its own stream during the timed
+steps) and the fp64 CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from head_latent_attention_decode_amd import mla  # noqa: E402
+from head_latent_attention_decode_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = ("decode attention GB/s and TFLOP/s (% of HBM/MFMA roofline); "
+          "µs per B×N×Skv step")
+SPLIT_SRC = os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", "mla_decode.hip")
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the method must move once: each KV row read once (all heads share
+    it), q, out (bf16), lse (fp32), the used page-table entries and the
+    lengths, plus the fp8 scale."""
+    esz = 1 if wl.cache_dtype == "fp8_e4m3fn" else 2
+    lens = wl.seq_lens.to(torch.int64)
+    kv = int(lens.sum()) * W.HEAD_SIZE * esz
+    pages = int(((lens + wl.page_size - 1) // wl.page_size).sum())
+    per_req = wl.N * W.HEAD_SIZE * 2 + wl.N * W.KV_LORA_RANK * 2 + wl.N * 4 + 4
+    return kv + wl.B * per_req + 4 * pages + (4 if esz == 1 else 0)
+
+
+def split_kernel_bytes(wl) -> int:
+    """Algorithmic bytes of the split kernel alone: KV rows, q, page-table
+    entries and lengths (its outputs are the partials, which are not
+    algorithmic)."""
+    esz = 1 if wl.cache_dtype == "fp8_e4m3fn" else 2
+    lens = wl.seq_lens.to(torch.int64)
+    pages = int(((lens + wl.page_size - 1) // wl.page_size).sum())
+    return (int(lens.sum()) * W.HEAD_SIZE * esz + wl.B * (wl.N * W.HEAD_SIZE * 2 + 4)
+            + 4 * pages)
+
+
+def algorithmic_flops(wl) -> int:
+    return 2 * (W.HEAD_SIZE + W.KV_LORA_RANK) * wl.N * wl.total_tokens()
+
+
+def source_hash() -> str:
+    with open(SPLIT_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM traffic per split-kernel launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_req: int):
+    """The fp64 oracle on the first n_req requests (all heads), on every host
+    core this process may use.  Returns the algorithmic GB/s of that sample."""
+    import oracle  # test infrastructure; only this leg of the benchmark uses it
+    cores = oracle.default_threads()
+    n_req = min(n_req, wl.B)
+    sub = W.Workload(name=wl.name, q=wl.q[:n_req], cache=wl.cache,
+                     block_table=wl.block_table[:n_req], seq_lens=wl.seq_lens[:n_req],
+                     softmax_scale=wl.softmax_scale, cache_scale=wl.cache_scale,
+                     cache_dtype=wl.cache_dtype, num_kv_splits=wl.num_kv_splits, seed=wl.seed)
+    prob = oracle.Problem(sub.q_float64(), sub.cache_bits(), sub.block_table.numpy(),
+                          sub.seq_lens.numpy(), sub.softmax_scale, cache_scale=sub.cache_scale)
+    t0 = time.perf_counter()
+    oracle.mla_decode(prob, nthreads=cores)
+    dt = time.perf_counter() - t0
+    gbs = algorithmic_bytes(sub) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_req} of {wl.B} requests, all {wl.N} heads, "
+                      f"{int(sub.seq_lens.sum())} KV tokens, {dt:.2f} s wall"}
+
+
+class Step:
+    """Pre-marshalled arguments of the two launches of one mla_decode call
+    (mla_decode_partials then mla_merge_states, exactly what mla_decode
+    enqueues), so the Python side adds as little as possible per step."""
+
+    def __init__(self, lib, d, wl, S, stream):
+        self.lib = lib
+        B, N = wl.B, wl.N
+        self.shape = mla.make_shape(d["q"], d["latent_cache"], d["block_table"], wl.cache_dtype)
+        nws = B * N * S * (W.KV_LORA_RANK + 1)
+        self.ws = torch.empty(nws, dtype=torch.float32, device=d["q"].device)
+        self.out = torch.empty((B, N, W.KV_LORA_RANK), dtype=torch.bfloat16, device=d["q"].device)
+        self.lse = torch.empty((B, N), dtype=torch.float32, device=d["q"].device)
+        vp = ctypes.c_void_p
+        part_lse = self.ws.data_ptr() + B * N * S * W.KV_LORA_RANK * 4
+        scale_ptr = vp(d["cache_scale"].data_ptr()) if d["cache_scale"] is not None else None
+        self.split_args = (ctypes.byref(self.shape), vp(d["q"].data_ptr()),
+                           vp(d["latent_cache"].data_ptr()), scale_ptr,
+                           vp(d["block_table"].data_ptr()), vp(d["seq_lens"].data_ptr()),
+                           ctypes.c_float(wl.softmax_scale), S, vp(self.ws.data_ptr()),
+                           nws * 4, vp(stream))
+        self.merge_args = (B * N, S, W.KV_LORA_RANK, vp(self.ws.data_ptr()), vp(part_lse),
+                           vp(self.out.data_ptr()), vp(self.lse.data_ptr()), vp(stream))
+
+    def split(self):
+        st = self.lib.mla_decode_partials(*self.split_args)
+        if st != 0:
+            raise mla.MLAError(st, "mla_decode_partials")
+
+    def merge(self):
+        st = self.lib.mla_merge_states(*self.merge_args)
+        if st != 0:
+            raise mla.MLAError(st, "mla_merge_states")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--splits", type=int, default=None, help="override num_kv_splits")
+    ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--cpu-requests", type=int, default=8,
+                    help="requests in the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": src.numel() * 4, "launches": 3}))
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported "
+              "(the decode path is built and measured on one MI355X; see DESIGN.md for how "
+              "it would shard)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = W.config_workload(args.workload)
+    S = args.splits or wl.num_kv_splits
+    lib = mla.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    copies = []
+    for _ in range(max(1, args.copies)):
+        d = dict(q=wl.q.to(dev), latent_cache=wl.cache.to(dev),
+                 block_table=wl.block_table.to(dev), seq_lens=wl.seq_lens.to(dev),
+                 cache_scale=(torch.tensor([wl.cache_scale], dtype=torch.float32, device=dev)
+                              if wl.cache_dtype == "fp8_e4m3fn" else None))
+        copies.append(Step(lib, d, wl, S, stream.cuda_stream))
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        st = copies[i % len(copies)]
+        st.split()
+        st.merge()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        st = copies[i % len(copies)]
+        ev[i][0].record(stream)
+        st.split()
+        ev[i][1].record(stream)
+        st.merge()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / K
+    split_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = algorithmic_bytes(wl)
+    flops = algorithmic_flops(wl)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    split_gbs = split_kernel_bytes(wl) / (split_ms * 1e-3) / 1e9
+    split_tflops = flops / (split_ms * 1e-3) / 1e12
+    # The split kernel is bound by HBM when its arithmetic intensity is below
+    # the bf16 ridge (312.5 flop/B), as for every bf16 workload here.
+    ai = flops / split_kernel_bytes(wl)
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(split_tflops, 1),
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(split_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = "mla_split_h128" if wl.N % 128 == 0 else "mla_split_h16"
+    roof["kernel_ms"] = round(split_ms, 5)
+
+    cpu = cpu_baseline(wl, args.cpu_requests) if args.cpu_requests > 0 else None
+    lens = wl.seq_lens
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "decode_tokens_per_s": round(wl.B / (ms_per_step * 1e-3), 1),
+        "kv_tokens_per_s": round(int(lens.sum()) / (ms_per_step * 1e-3), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cache_dtype == "bf16" else "fp8_e4m3fn cache, bf16 MFMA",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B} requests x N={wl.N} heads, "
+                               f"KV lengths {int(lens.min())}..{int(lens.max())}, "
+                               f"page {wl.page_size}, num_kv_splits={S}, "
+                               f"{wl.cache_dtype} cache, q/row width 576, value width 512",
+                   "batch": wl.B, "num_heads": wl.N, "kv_tokens": int(lens.sum()),
+                   "num_kv_splits": S, "page_size": wl.page_size,
+                   "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                   "input_copies_rotated": len(copies)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

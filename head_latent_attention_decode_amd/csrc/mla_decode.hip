@@ -38,6 +38,7 @@
 //    bf16 output directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "mla_decode.h"
 
@@ -64,6 +65,17 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define AS3(ptr) ((LDS_AS uint8_t *)(ptr))
+#define CONST_AS __attribute__((address_space(4)))
+
+// Read-only, wave-uniform data (page table entries, lengths, the fp8 scale)
+// is read through the constant address space so that it becomes a scalar
+// load: scalar loads are tracked by lgkmcnt, so they never force a wait on
+// the vector-memory counter that tracks the tile loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *p, long long i)
+{
+    return ((const CONST_AS T *)p)[i];
+}
 
 struct Params {
     const __bf16 *q;            // [B, N, 576]
@@ -79,12 +91,16 @@ struct Params {
     int B, N, S, MB, num_blocks, page_shift, HG;
 };
 
-// XOR swizzle of the 16-byte chunks of LDS row r.  Rows r..r+7 then place a
-// given chunk in 8 different bank groups (MFMA operand reads, 8 lanes a
-// pass), and rows 4a..4a+3 place an aligned 32-byte chunk pair in 4 different
-// 32-byte bank groups (transposed reads, 16 lanes a pass).  The XOR stays
-// inside an aligned group of 8 chunks, so it never leaves the 72-chunk row.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// XOR swizzle of the 16-byte chunks of LDS row r (rows are 1152 bytes):
+// logical chunk c of row r is stored at chunk c ^ swz(r), where swz(r) swaps
+// bits 1 and 2 of r & 7.  With gfx950's 64 four-byte banks this makes both
+// read patterns of a tile conflict-free (measured with the LDS bank-conflict
+// counter on every candidate linear swizzle of the low row bits): the
+// ds_read_b128 operand reads of QK^T (16 consecutive rows, one chunk each)
+// and the ds_read_b64_tr_b16 transposed reads of PV (16-lane groups reading
+// 4 consecutive rows x 32 bytes).  The XOR stays inside an aligned group of 8
+// chunks, so it never leaves the 72-chunk row, and it depends on r & 7 only.
+__device__ __forceinline__ int swz(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
 
 // Workgroup id -> (request, split, head group).  The hardware deals
 // consecutive workgroup ids round-robin over the 8 XCDs; when the grid is a
@@ -106,7 +122,7 @@ __device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int
 __device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &t0, int &t1)
 {
     const long long cap = (long long)p.MB << p.page_shift;
-    long long L = p.seq_lens[b];
+    long long L = load_uniform(p.seq_lens, b);
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const long long per = (L + p.S - 1) / p.S;
     const long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
@@ -119,6 +135,33 @@ __device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks)
 {
     return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+}
+
+// Page-table window of one wave: lane i holds the block id of logical page
+// base + i of request b, so a tile's block id is one v_readlane away and the
+// tile loop issues no memory access for the page table.  Pages only move
+// forward within a split, and the window is refilled (a vector load) once
+// every 64 pages; the compiler waits for that load before the readlane.
+struct PageWindow {
+    int base;         // first logical page held (wave-uniform)
+    int ids;          // this lane's entry
+};
+
+__device__ __forceinline__ void window_fill(const Params &p, PageWindow &win, int b, int page,
+                                            int lane)
+{
+    win.base = page;
+    int idx = page + lane;
+    idx = idx < p.MB ? idx : p.MB - 1;
+    win.ids = p.block_table[(long long)b * p.MB + idx];
+}
+
+__device__ __forceinline__ int window_block(const Params &p, PageWindow &win, int b, int page,
+                                            int lane)
+{
+    if (page - win.base >= 64)
+        window_fill(p, win, b, page, lane);
+    return clamp_block(__builtin_amdgcn_readlane(win.ids, page - win.base), p.num_blocks);
 }
 
 // Wait until at most n vector-memory operations of this wave are in flight
@@ -194,8 +237,9 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned v)
 }
 
 // ===========================================================================
-// 128 heads per workgroup: 8 waves (two per SIMD), 32-token tiles shared by
-// all waves through an LDS ring.
+// Wide kernel: 32 * NG heads per workgroup, 2 * NG waves, 32-token tiles
+// shared by all waves through an LDS ring (NG = 2: 4 waves, one per SIMD,
+// 64 heads; NG = 4: 8 waves, two per SIMD, 128 heads).
 //   wave w = (g, c), g = w / 2 picks a group of 32 heads, c = w % 2 a half.
 //   QK^T: the wave scores heads 32g + 16c .. +16 over all 32 tokens
 //         (v_mfma_f32_16x16x32_bf16, S^T = K . Q^T, 72 VGPRs of query).
@@ -213,26 +257,48 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned v)
 constexpr int kT32 = 32;                        // tokens per tile
 constexpr int kStage32 = kT32 * kRowBytes;      // 36864 bytes (bf16 tile)
 constexpr int kStage8 = kT32 * kRowBytes8;      // 18432 bytes (fp8 tile)
-constexpr int kPbufBytes = 4 * 32 * 32 * 2;     // [group][head][token] bf16
-constexpr int kAbufBytes = 4 * 32 * 4;          // [group][head] float
+constexpr int kPbufRow = 80;                    // bytes per head row (64 + 16 pad)
+constexpr int kGroupPbuf = 32 * kPbufRow;       // [head][token] bf16 per group
 
-template <bool kFp8>
-struct H128Layout {
+template <int NG, bool kFp8>
+struct WideCfg {
+    static constexpr int kWaves = 2 * NG;
+    static constexpr int kThreads = 64 * kWaves;
+    // DMA instructions (64 lanes x 16 bytes) per tile, spread over the waves:
+    // wave w issues instructions w, w + kWaves, ...
+    static constexpr int kDma = kFp8 ? kStage8 / 1024 : kStage32 / 1024;   // 18 or 36
+    static constexpr int kDmaLo = kDma / kWaves;           // per wave, rounded down
+    static constexpr int kDmaHiWaves = kDma % kWaves;      // waves issuing one more
     static constexpr int kBf16Stages = kFp8 ? 2 : 4;
     static constexpr int kStaging = kBf16Stages * kStage32;          // fp8 staging offset
     static constexpr int kPbuf = kStaging + (kFp8 ? 3 * kStage8 : 0);
-    static constexpr int kAbuf = kPbuf + kPbufBytes;
-    static constexpr int kTotal = kAbuf + kAbufBytes;
+    static constexpr int kAbuf = kPbuf + NG * kGroupPbuf;
+    static constexpr int kLds = kAbuf + NG * 32 * 4;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
 };
-static_assert(H128Layout<false>::kTotal <= 160 * 1024, "LDS budget");
-static_assert(H128Layout<true>::kTotal <= 160 * 1024, "LDS budget");
 
-// bf16 tile: 36 DMA instructions; wave w takes i = w, w+8, ... (5 for waves
-// 0-3, 4 for waves 4-7).  Instruction i fills LDS chunks [64i, 64i+64) of the
-// tile: rows of the half h = i / 18 (rows 16h .. 16h+15), which lie in one
-// page.  Logical chunk c of row r is stored at chunk c ^ swz(r).
-__device__ __forceinline__ void issue_tile32(const Params &p, LDS_AS uint8_t *stage, int w,
-                                             int lane, int b, int tile_start, int t_end)
+// Wait until this wave has at most `k` tiles (k = 0, 1, 2) of loads in flight.
+template <int n>
+__device__ __forceinline__ void wait_k_tiles(int k)
+{
+    if (k >= 2) wait_vmcnt<2 * n>(); else if (k == 1) wait_vmcnt<n>(); else wait_vmcnt<0>();
+}
+template <class Cfg>
+__device__ __forceinline__ void wait_tiles_wide(int w, int k)
+{
+    if (Cfg::kDmaHiWaves != 0 && w < Cfg::kDmaHiWaves)
+        wait_k_tiles<Cfg::kDmaLo + 1>(k);
+    else
+        wait_k_tiles<Cfg::kDmaLo>(k);
+}
+
+// bf16 tile: instruction i fills LDS chunks [64i, 64i+64) of the tile, i.e.
+// rows of the half h = i / 18 (rows 16h .. 16h+15), which lie in one page.
+// Logical chunk c of row r is stored at chunk c ^ swz(r).
+template <class Cfg>
+__device__ __forceinline__ void issue_tile_wide(const Params &p, PageWindow &win,
+                                                LDS_AS uint8_t *stage, int w, int lane, int b,
+                                                int tile_start, int t_end)
 {
     const int last = t_end - 1;
     const int pmask = (1 << p.page_shift) - 1;
@@ -241,13 +307,12 @@ __device__ __forceinline__ void issue_tile32(const Params &p, LDS_AS uint8_t *st
     for (int h = 0; h < 2; ++h) {
         int first = tile_start + 16 * h;
         first = first < last ? first : last;
-        const int blk = clamp_block(p.block_table[(long long)b * p.MB + (first >> p.page_shift)],
-                                    p.num_blocks);
+        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
         base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes;
     }
 #pragma unroll
-    for (int m = 0; m < 5; ++m) {
-        const int i = w + 8 * m;
+    for (int m = 0; m < (36 + Cfg::kWaves - 1) / Cfg::kWaves; ++m) {
+        const int i = w + Cfg::kWaves * m;
         if (i < 36) {
             const int q = i * 64 + lane;
             const int r = q / kRowChunks;
@@ -259,11 +324,12 @@ __device__ __forceinline__ void issue_tile32(const Params &p, LDS_AS uint8_t *st
     }
 }
 
-// fp8 tile: 18 DMA instructions (3 for waves 0-1, 2 for waves 2-7) into an
-// unswizzled staging buffer of 576-byte rows; instruction i covers rows of
-// the half i / 9.
-__device__ __forceinline__ void issue_tile32_fp8(const Params &p, LDS_AS uint8_t *stg, int w,
-                                                 int lane, int b, int tile_start, int t_end)
+// fp8 tile: 18 DMA instructions into an unswizzled staging buffer of 576-byte
+// rows; instruction i covers rows of the half i / 9.
+template <class Cfg>
+__device__ __forceinline__ void issue_tile_wide_fp8(const Params &p, PageWindow &win,
+                                                    LDS_AS uint8_t *stg, int w, int lane, int b,
+                                                    int tile_start, int t_end)
 {
     const int last = t_end - 1;
     const int pmask = (1 << p.page_shift) - 1;
@@ -272,13 +338,12 @@ __device__ __forceinline__ void issue_tile32_fp8(const Params &p, LDS_AS uint8_t
     for (int h = 0; h < 2; ++h) {
         int first = tile_start + 16 * h;
         first = first < last ? first : last;
-        const int blk = clamp_block(p.block_table[(long long)b * p.MB + (first >> p.page_shift)],
-                                    p.num_blocks);
+        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
         base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
     }
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-        const int i = w + 8 * m;
+    for (int m = 0; m < (18 + Cfg::kWaves - 1) / Cfg::kWaves; ++m) {
+        const int i = w + Cfg::kWaves * m;
         if (i < 18) {
             const int q = i * 64 + lane;
             const int r = q / kRowChunks8;
@@ -290,14 +355,15 @@ __device__ __forceinline__ void issue_tile32_fp8(const Params &p, LDS_AS uint8_t
     }
 }
 
-// Widen a staged fp8 tile into a swizzled bf16 stage: 512 threads, 9 groups
-// of 4 bytes each.
-__device__ __forceinline__ void convert_tile32(const LDS_AS uint8_t *stg, LDS_AS uint8_t *stage,
-                                               int tid)
+// Widen a staged fp8 tile into a swizzled bf16 stage: 4608 groups of 4 bytes
+// spread over the workgroup's threads.
+template <class Cfg>
+__device__ __forceinline__ void convert_tile_wide(const LDS_AS uint8_t *stg, LDS_AS uint8_t *stage,
+                                                  int tid)
 {
-#pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int e = m * 512 + tid;
+#pragma unroll 3
+    for (int m = 0; m < 4608 / Cfg::kThreads; ++m) {
+        const int e = m * Cfg::kThreads + tid;
         const int r = e / 144, c4 = e % 144;
         const unsigned v = *(const LDS_AS unsigned *)(stg + r * kRowBytes8 + c4 * 4);
         *(LDS_AS u32x2 *)(stage + r * kRowBytes + ((c4 >> 1) ^ swz(r)) * 16 + (c4 & 1) * 8) =
@@ -305,32 +371,13 @@ __device__ __forceinline__ void convert_tile32(const LDS_AS uint8_t *stg, LDS_AS
     }
 }
 
-// Wait until this wave has at most `k` tiles (k = 0, 1, 2) of loads in flight.
-template <bool kFp8>
-__device__ __forceinline__ void wait_tiles128(int w, int k)
-{
-    if (kFp8) {
-        if (w < 2) {
-            if (k >= 2) wait_vmcnt<6>(); else if (k == 1) wait_vmcnt<3>(); else wait_vmcnt<0>();
-        } else {
-            if (k >= 2) wait_vmcnt<4>(); else if (k == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
-        }
-    } else {
-        if (w < 4) {
-            if (k >= 2) wait_vmcnt<10>(); else if (k == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
-        } else {
-            if (k >= 2) wait_vmcnt<8>(); else if (k == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-        }
-    }
-}
-
-struct State128 {
+struct StateWide {
     f32x16 o[8];      // O^T: 8 blocks of 32 output columns x 32 heads
     float m;          // running max (log2) of the wave's 16 QK heads
     float l;          // this lane's share of their row sums
 };
 
-struct Lane128 {
+struct LaneWide {
     int c, r16, g4, r32, g2;
     int ko[2];        // QK A-operand offsets (k even / odd)
     int to[2][2];     // PV transposed-read offsets [half][cb parity]
@@ -338,22 +385,40 @@ struct Lane128 {
 
 // One 32-token tile: scores, online softmax, probability exchange, PV.
 // Contains one workgroup barrier (after the probabilities are written).
-__device__ __forceinline__ void tile128(State128 &st, const bf16x8 (&qf)[18],
-                                        const LDS_AS uint8_t *stage, LDS_AS uint8_t *pbuf,
-                                        LDS_AS float *abuf, const Lane128 &ln, float scale_log2,
-                                        int tile_start, int t_end)
+__device__ __forceinline__ void tile_wide(StateWide &st, const bf16x8 (&qf)[18],
+                                          const LDS_AS uint8_t *stage, LDS_AS uint8_t *pbuf,
+                                          LDS_AS float *abuf, const LaneWide &ln, float scale_log2,
+                                          int tile_start, int t_end)
 {
-    // ---- S^T[token][head] for 2 blocks of 16 tokens x this wave's 16 heads
-    f32x4 sc[2] = {f32x4{}, f32x4{}};
+    // ---- S^T[token][head] for 2 blocks of 16 tokens x this wave's 16 heads.
+    // Fragment j = 2k + tb; LDS reads run kQkAhead fragments ahead of the
+    // MFMAs that consume them (one LDS read per MFMA).
+    constexpr int kQkAhead = 4;
+    auto kfrag = [&](int j) {
+        const int k = j >> 1, tb = j & 1;
+        return *(const LDS_AS bf16x8 *)(stage + ln.ko[k & 1] + (k >> 1) * 128 +
+                                        tb * 16 * kRowBytes);
+    };
+    // Four accumulator chains (token block x parity of k) keep consecutive
+    // MFMAs independent; they are summed after the loop.
+    f32x4 sc4[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    bf16x8 kb[kQkAhead];
 #pragma unroll
-    for (int k = 0; k < 18; ++k) {
+    for (int j = 0; j < kQkAhead; ++j)
+        kb[j] = kfrag(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);   // the first reads
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const bf16x8 a = *(const LDS_AS bf16x8 *)(stage + ln.ko[k & 1] + (k >> 1) * 128 +
-                                                      tb * 16 * kRowBytes);
-            sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k], sc[tb], 0, 0, 0);
-        }
+    for (int j = 0; j < 36; ++j) {
+        const bf16x8 a = kb[j % kQkAhead];
+        if (j + kQkAhead < 36)
+            kb[j % kQkAhead] = kfrag(j + kQkAhead);
+        sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j >> 1], sc4[j & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA j
+        if (j + kQkAhead < 36)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read j + kQkAhead
     }
+    // j & 3 = tb + 2 * (k & 1): chains 0, 2 hold token block 0, chains 1, 3 block 1
+    const f32x4 sc[2] = {sc4[0] + sc4[2], sc4[1] + sc4[3]};
     // ---- mask, scale, lazy online softmax of the wave's 16 heads
     float x[8];
     float mx = -INFINITY;
@@ -384,7 +449,7 @@ __device__ __forceinline__ void tile128(State128 &st, const bf16x8 (&qf)[18],
                                      __builtin_amdgcn_exp2f(x[4 * tb + 3] - st.m));
         lsum += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
         // P[head 16c + r16][tokens 16tb + 4g4 .. +4]
-        *(LDS_AS bf16x4 *)(pbuf + (16 * ln.c + ln.r16) * 64 + (16 * tb + 4 * ln.g4) * 2) =
+        *(LDS_AS bf16x4 *)(pbuf + (16 * ln.c + ln.r16) * kPbufRow + (16 * tb + 4 * ln.g4) * 2) =
             bf16x4{p01[0], p01[1], p23[0], p23[1]};
     }
     st.l += lsum;
@@ -402,27 +467,42 @@ __device__ __forceinline__ void tile128(State128 &st, const bf16x8 (&qf)[18],
     bf16x8 pf[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-        pf[kk] = *(const LDS_AS bf16x8 *)(pbuf + ln.r32 * 64 + (16 * kk + 8 * ln.g2) * 2);
+        pf[kk] = *(const LDS_AS bf16x8 *)(pbuf + ln.r32 * kPbufRow + (16 * kk + 8 * ln.g2) * 2);
+    // V^T fragment j = cb + 8kk: two transposed reads; kept kPvAhead
+    // fragments ahead of the MFMAs.  Consecutive MFMAs go to different
+    // accumulators (the two k-steps of a column block are 8 MFMAs apart).
+    constexpr int kPvAhead = 3;
+    auto vfrag = [&](int j) {
+        const int cb = j & 7, kk = j >> 3;
+        const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(stage + ln.to[0][cb & 1] + off));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(stage + ln.to[1][cb & 1] + off));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 vb[kPvAhead];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
+    for (int j = 0; j < kPvAhead; ++j)
+        vb[j] = vfrag(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead + 2, 0);  // P^T + first V^T
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4 *)(stage + ln.to[0][cb & 1] + off));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4 *)(stage + ln.to[1][cb & 1] + off));
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], st.o[cb], 0, 0, 0);
-        }
+    for (int j = 0; j < 16; ++j) {
+        const bf16x8 a = vb[j % kPvAhead];
+        if (j + kPvAhead < 16)
+            vb[j % kPvAhead] = vfrag(j + kPvAhead);
+        st.o[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j >> 3], st.o[j & 7], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA j
+        if (j + kPvAhead < 16)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of j + kPvAhead
     }
 }
 
-template <bool kDirect, bool kFp8>
-__global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
+template <int NG, bool kDirect, bool kFp8>
+__global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
 {
-    using Lay = H128Layout<kFp8>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lay::kTotal];
+    using Cfg = WideCfg<NG, kFp8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLds];
 
     int b, s, hg;
     decode_work(p, b, s, hg);
@@ -432,18 +512,20 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = w >> 1;
-    Lane128 ln;
+    LaneWide ln;
     ln.c = w & 1;
     ln.r16 = lane & 15;
     ln.g4 = lane >> 4;
     ln.r32 = lane & 31;
     ln.g2 = lane >> 5;
-    const long long head0 = (long long)b * p.N + hg * 128;       // row of head 0
+    const int HB = 32 * NG;                                       // heads per workgroup
+    const long long head0 = (long long)b * p.N + hg * HB;        // row of head 0
     const long long qrow = head0 + 32 * g + 16 * ln.c + ln.r16;   // QK head
     const long long orow = head0 + 32 * g + ln.r32;               // PV head
 
     if (t_begin >= t_end) {
-        // empty split: (0, -inf), or out = 0 / lse = -inf when direct
+        // empty split: (0, -inf), or out = 0 / lse = -inf when direct.
+        // Each thread clears 512 * HB / kThreads = 128 columns of one head.
         const int hh = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 128;
         if (kDirect) {
             __bf16 *o = p.out + (head0 + hh) * kDV + c0;
@@ -462,8 +544,8 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
     }
 
     LDS_AS uint8_t *lds = AS3(smem);
-    LDS_AS uint8_t *pbuf = lds + Lay::kPbuf + g * (32 * 32 * 2);
-    LDS_AS float *abuf = (LDS_AS float *)(lds + Lay::kAbuf) + g * 32;
+    LDS_AS uint8_t *pbuf = lds + Cfg::kPbuf + g * kGroupPbuf;
+    LDS_AS float *abuf = (LDS_AS float *)(lds + Cfg::kAbuf) + g * 32;
 
     // QK A operand: row 16tb + r16, logical chunk 4k + g4
 #pragma unroll
@@ -487,7 +569,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
     float scale_log2 = p.scale_log2;
     float out_scale = 1.0f;
     if (kFp8) {
-        const float ks = *p.cache_scale;
+        const float ks = load_uniform(p.cache_scale, 0);
         scale_log2 *= ks;
         out_scale = ks;
     }
@@ -502,9 +584,11 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
         for (int k = 0; k < 18; ++k)
             qf[k] = *(const bf16x8 *)(qp + 32 * k);
     }
+    PageWindow win;
+    window_fill(p, win, b, t_begin >> p.page_shift, lane);
     wait_vmcnt<0>();
 
-    State128 st;
+    StateWide st;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
         st.o[cb] = f32x16{};
@@ -516,34 +600,35 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
 #pragma unroll
         for (int t = 0; t < 3; ++t)
             if (t < ntiles)
-                issue_tile32(p, lds + t * kStage32, w, lane, b, t_begin + t * kT32, t_end);
+                issue_tile_wide<Cfg>(p, win, lds + t * kStage32, w, lane, b, t_begin + t * kT32, t_end);
         for (int t = 0; t < ntiles; ++t) {
             // Wait for this wave's loads of tile t (t+1, t+2 may stay in
             // flight); the barrier then makes every wave's loads visible and
             // guarantees stage (t+3)%4 = (t-1)%4 and the probability buffer
             // are no longer read.
             const int after = ntiles - 1 - t;
-            wait_tiles128<false>(w, after < 2 ? after : 2);
+            wait_tiles_wide<Cfg>(w, after < 2 ? after : 2);
             barrier_no_fence();
             if (t + 3 < ntiles)
-                issue_tile32(p, lds + ((t + 3) & 3) * kStage32, w, lane, b,
-                             t_begin + (t + 3) * kT32, t_end);
-            tile128(st, qf, lds + (t & 3) * kStage32, pbuf, abuf, ln, scale_log2,
-                    t_begin + t * kT32, t_end);
+                issue_tile_wide<Cfg>(p, win, lds + ((t + 3) & 3) * kStage32, w, lane, b,
+                                     t_begin + (t + 3) * kT32, t_end);
+            tile_wide(st, qf, lds + (t & 3) * kStage32, pbuf, abuf, ln, scale_log2,
+                      t_begin + t * kT32, t_end);
         }
     } else {
-        LDS_AS uint8_t *stg = lds + Lay::kStaging;
+        LDS_AS uint8_t *stg = lds + Cfg::kStaging;
         const int tid = threadIdx.x;
 #pragma unroll
         for (int t = 0; t < 3; ++t)
             if (t < ntiles)
-                issue_tile32_fp8(p, stg + t * kStage8, w, lane, b, t_begin + t * kT32, t_end);
-        wait_tiles128<true>(w, ntiles - 1 < 2 ? ntiles - 1 : 2);
+                issue_tile_wide_fp8<Cfg>(p, win, stg + t * kStage8, w, lane, b, t_begin + t * kT32,
+                                         t_end);
+        wait_tiles_wide<Cfg>(w, ntiles - 1 < 2 ? ntiles - 1 : 2);
         barrier_no_fence();
-        convert_tile32(stg, lds, tid);
+        convert_tile_wide<Cfg>(stg, lds, tid);
         barrier_no_fence();
         if (3 < ntiles)
-            issue_tile32_fp8(p, stg, w, lane, b, t_begin + 3 * kT32, t_end);
+            issue_tile_wide_fp8<Cfg>(p, win, stg, w, lane, b, t_begin + 3 * kT32, t_end);
         for (int t = 0; t < ntiles; ++t) {
             if (t + 1 < ntiles) {
                 // fp8 tile t+1 -> bf16 stage (t+1)%2; tiles t+2, t+3 may stay
@@ -551,16 +636,17 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
                 // that stage; the second retires the staging buffer, which is
                 // refilled with tile t+4.
                 const int after = ntiles - 2 - t;
-                wait_tiles128<true>(w, after < 2 ? after : 2);
+                wait_tiles_wide<Cfg>(w, after < 2 ? after : 2);
                 barrier_no_fence();
-                convert_tile32(stg + ((t + 1) % 3) * kStage8, lds + ((t + 1) & 1) * kStage32, tid);
+                convert_tile_wide<Cfg>(stg + ((t + 1) % 3) * kStage8,
+                                       lds + ((t + 1) & 1) * kStage32, tid);
                 barrier_no_fence();
                 if (t + 4 < ntiles)
-                    issue_tile32_fp8(p, stg + ((t + 1) % 3) * kStage8, w, lane, b,
-                                     t_begin + (t + 4) * kT32, t_end);
+                    issue_tile_wide_fp8<Cfg>(p, win, stg + ((t + 1) % 3) * kStage8, w, lane, b,
+                                             t_begin + (t + 4) * kT32, t_end);
             }
-            tile128(st, qf, lds + (t & 1) * kStage32, pbuf, abuf, ln, scale_log2,
-                    t_begin + t * kT32, t_end);
+            tile_wide(st, qf, lds + (t & 1) * kStage32, pbuf, abuf, ln, scale_log2,
+                      t_begin + t * kT32, t_end);
         }
     }
 
@@ -568,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_h128(Params p)
     float ltot = st.l + __shfl_xor(st.l, 16);
     ltot += __shfl_xor(ltot, 32);
     barrier_no_fence();   // every wave is done with pbuf / abuf
-    LDS_AS float *mbuf = (LDS_AS float *)(lds + Lay::kPbuf) + g * 64;
+    LDS_AS float *mbuf = (LDS_AS float *)(lds + Cfg::kPbuf) + g * 64;
     if (ln.g4 == 0) {
         mbuf[16 * ln.c + ln.r16] = st.m;
         mbuf[32 + 16 * ln.c + ln.r16] = ltot;
@@ -623,12 +709,13 @@ constexpr int kWaveLds16 = 2 * kStage16;                   // 36864 bytes per wa
 constexpr int kLoadsPerTile16 = kT16 * kRowChunks / 64;    // 18 DMA ops (bf16)
 constexpr int kLoadsPerTile16f8 = kT16 * kRowChunks8 / 64; // 9 DMA ops (fp8)
 
-__device__ __forceinline__ void issue_tile16(const Params &p, LDS_AS uint8_t *stage, int lane,
-                                             int b, int tile_start, int t_end)
+__device__ __forceinline__ void issue_tile16(const Params &p, PageWindow &win,
+                                             LDS_AS uint8_t *stage, int lane, int b,
+                                             int tile_start, int t_end)
 {
     const int last = t_end - 1;
     const int page = tile_start >> p.page_shift;   // 16-aligned tile: one page
-    const int blk = clamp_block(p.block_table[(long long)b * p.MB + page], p.num_blocks);
+    const int blk = window_block(p, win, b, page, lane);
     const int pmask = (1 << p.page_shift) - 1;
     const uint8_t *base = p.cache + ((long long)blk << p.page_shift) * kRowBytes;
 #pragma unroll
@@ -642,12 +729,13 @@ __device__ __forceinline__ void issue_tile16(const Params &p, LDS_AS uint8_t *st
     }
 }
 
-__device__ __forceinline__ void issue_tile16_fp8(const Params &p, LDS_AS uint8_t *stg, int lane,
-                                                 int b, int tile_start, int t_end)
+__device__ __forceinline__ void issue_tile16_fp8(const Params &p, PageWindow &win,
+                                                 LDS_AS uint8_t *stg, int lane, int b,
+                                                 int tile_start, int t_end)
 {
     const int last = t_end - 1;
     const int page = tile_start >> p.page_shift;
-    const int blk = clamp_block(p.block_table[(long long)b * p.MB + page], p.num_blocks);
+    const int blk = window_block(p, win, b, page, lane);
     const int pmask = (1 << p.page_shift) - 1;
     const uint8_t *base = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
 #pragma unroll
@@ -794,7 +882,7 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
     float scale_log2 = p.scale_log2;
     float out_scale = 1.0f;
     if (kFp8) {
-        const float ks = *p.cache_scale;
+        const float ks = load_uniform(p.cache_scale, 0);
         scale_log2 *= ks;
         out_scale = ks;
     }
@@ -808,6 +896,8 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
         for (int k = 0; k < 18; ++k)
             qf[k] = *(const bf16x8 *)(qrow + 32 * k);
     }
+    PageWindow win;
+    window_fill(p, win, b, (t_begin + w * kT16) >> p.page_shift, lane);
     wait_vmcnt<0>();
 
     State16 st;
@@ -823,11 +913,11 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
     if (!kFp8) {
         LDS_AS uint8_t *sa = mine_lds, *sb = mine_lds + kStage16;
         if (mine > 0)
-            issue_tile16(p, sa, lane, b, t_begin + w * kT16, t_end);
+            issue_tile16(p, win, sa, lane, b, t_begin + w * kT16, t_end);
         for (int i = 0; i < mine; i += 2) {
             const int tA = t_begin + (w + 4 * i) * kT16;
             if (i + 1 < mine) {
-                issue_tile16(p, sb, lane, b, tA + 4 * kT16, t_end);
+                issue_tile16(p, win, sb, lane, b, tA + 4 * kT16, t_end);
                 wait_vmcnt<kLoadsPerTile16>();
             } else {
                 wait_vmcnt<0>();
@@ -836,7 +926,7 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
             if (i + 1 >= mine)
                 break;
             if (i + 2 < mine) {
-                issue_tile16(p, sa, lane, b, tA + 8 * kT16, t_end);
+                issue_tile16(p, win, sa, lane, b, tA + 8 * kT16, t_end);
                 wait_vmcnt<kLoadsPerTile16>();
             } else {
                 wait_vmcnt<0>();
@@ -847,9 +937,9 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
         LDS_AS uint8_t *bst = mine_lds;
         LDS_AS uint8_t *stg[2] = {mine_lds + kStage16, mine_lds + kStage16 + kStage16f8};
         if (mine > 0)
-            issue_tile16_fp8(p, stg[0], lane, b, t_begin + w * kT16, t_end);
+            issue_tile16_fp8(p, win, stg[0], lane, b, t_begin + w * kT16, t_end);
         if (mine > 1)
-            issue_tile16_fp8(p, stg[1], lane, b, t_begin + (w + 4) * kT16, t_end);
+            issue_tile16_fp8(p, win, stg[1], lane, b, t_begin + (w + 4) * kT16, t_end);
         for (int i = 0; i < mine; ++i) {
             if (i + 1 < mine)
                 wait_vmcnt<kLoadsPerTile16f8>();
@@ -857,7 +947,7 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
                 wait_vmcnt<0>();
             convert_tile16(stg[i & 1], bst, lane);
             if (i + 2 < mine)
-                issue_tile16_fp8(p, stg[i & 1], lane, b, t_begin + (w + 4 * (i + 2)) * kT16,
+                issue_tile16_fp8(p, win, stg[i & 1], lane, b, t_begin + (w + 4 * (i + 2)) * kT16,
                                  t_end);
             compute_tile16(scale_log2, st, qf, bst, ko, vo, lane,
                            t_begin + (w + 4 * i) * kT16, t_end);
@@ -1040,24 +1130,40 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     p.num_blocks = s->num_blocks;
     p.page_shift = log2_int(s->page_size);
     const bool direct = part_out == nullptr;
-    const bool wide = s->num_heads % 128 == 0;
-    p.HG = wide ? s->num_heads / 128 : s->num_heads / 16;
+    const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
+    // Head-group size of the wide kernel: 64 heads (4 waves, one per SIMD)
+    // unless MLA_DECODE_WG_HEADS=128 selects 128 heads (8 waves) for
+    // experiments.  Head counts that are not multiples of 64 use the 16-head
+    // kernel.
+    static const int wg_heads = [] {
+        const char *e = getenv("MLA_DECODE_WG_HEADS");
+        return (e && atoi(e) == 128) ? 128 : 64;
+    }();
+    int kind;   // 0: 16 heads, 1: 64 heads, 2: 128 heads per workgroup
+    if (s->num_heads % 128 == 0 && wg_heads == 128)
+        kind = 2;
+    else if (s->num_heads % 64 == 0)
+        kind = 1;
+    else
+        kind = 0;
+    p.HG = s->num_heads / (kind == 2 ? 128 : kind == 1 ? 64 : 16);
     const long long grid = (long long)s->batch * S * p.HG;
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
-    dim3 g((unsigned)grid), blk(wide ? 512 : 256);
-    const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
-#define MLA_LAUNCH(KERNEL)                                                              \
-    do {                                                                                \
-        if (direct && fp8) hipLaunchKernelGGL((KERNEL<true, true>), g, blk, 0, stream, p);    \
-        else if (direct) hipLaunchKernelGGL((KERNEL<true, false>), g, blk, 0, stream, p);     \
-        else if (fp8) hipLaunchKernelGGL((KERNEL<false, true>), g, blk, 0, stream, p);        \
-        else hipLaunchKernelGGL((KERNEL<false, false>), g, blk, 0, stream, p);                \
+    dim3 g((unsigned)grid), blk(kind == 2 ? 512 : 256);
+#define MLA_LAUNCH(...)                                                                         \
+    do {                                                                                        \
+        if (direct && fp8) hipLaunchKernelGGL((__VA_ARGS__ true, true>), g, blk, 0, stream, p);    \
+        else if (direct) hipLaunchKernelGGL((__VA_ARGS__ true, false>), g, blk, 0, stream, p);     \
+        else if (fp8) hipLaunchKernelGGL((__VA_ARGS__ false, true>), g, blk, 0, stream, p);        \
+        else hipLaunchKernelGGL((__VA_ARGS__ false, false>), g, blk, 0, stream, p);                \
     } while (0)
-    if (wide)
-        MLA_LAUNCH(mla_split_h128);
+    if (kind == 2)
+        MLA_LAUNCH(mla_split_wide<4,);
+    else if (kind == 1)
+        MLA_LAUNCH(mla_split_wide<2,);
     else
-        MLA_LAUNCH(mla_split_h16);
+        MLA_LAUNCH(mla_split_h16<);
 #undef MLA_LAUNCH
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

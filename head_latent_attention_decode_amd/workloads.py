@@ -91,7 +91,7 @@ class Workload:
 CONFIGS = {
     "tiny": dict(B=2, N=16, page_size=16, seq_lens=[37, 100], num_kv_splits=4,
                  cache_dtype="bf16", seed=1),
-    "dsv3": dict(B=64, N=128, page_size=64, seq_lens=[4096] * 64, num_kv_splits=4,
+    "dsv3": dict(B=64, N=128, page_size=64, seq_lens=[4096] * 64, num_kv_splits=2,
                  cache_dtype="bf16", seed=2),
     "ragged": dict(B=128, N=128, page_size=64, seq_lens="uniform:1:32768",
                    num_kv_splits=32, cache_dtype="bf16", seed=3, max_len=32768),
