@@ -4,7 +4,7 @@
 A step is one mla_decode call (split kernel + LSE-merge kernel) over one
 batch of the DeepSeek-V3-shaped decode workload: B = 64 requests, N = 128
 heads, 4096 cached tokens each, page size 64, bf16 query and cache,
-num_kv_splits = 4.  Inputs are synthetic (seeded), generated on the host and
+num_kv_splits = 2 (other shapes via --workload).  Inputs are synthetic (seeded), generated on the host and
 resident in HBM before the timed region; three copies of the query, cache
 and page table are rotated so that no step finds its KV rows in the 256 MB
 Infinity Cache left behind by the previous step.
@@ -22,6 +22,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -68,23 +69,32 @@ def algorithmic_flops(wl) -> int:
     return 2 * (W.HEAD_SIZE + W.KV_LORA_RANK) * wl.N * wl.total_tokens()
 
 
+def split_kernel_name(wl) -> str:
+    """Symbol prefix of the split kernel the library launches for this shape:
+    the 64-head workgroup kernel when N is a multiple of 64, else the 16-head
+    one."""
+    return "mla_split_wide" if wl.N % 64 == 0 else "mla_split_h16"
+
+
 def source_hash() -> str:
     with open(SPLIT_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM traffic per split-kernel launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_traffic.json")
+def measured_traffic(wl):
+    """HBM bytes per split-kernel launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy-kernel calibration) from the committed counter summary
+    for this kernel and workload, if it was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"{split_kernel_name(wl)}_{wl.name}_traffic.md")
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+    except OSError:
         return None
-    if rec.get("source_sha256_16") != source_hash():
+    fields = dict(re.findall(r"^(source_sha256_16|hbm_bytes_per_launch) = (\S+)$", text, re.M))
+    if fields.get("source_sha256_16") != source_hash() or "hbm_bytes_per_launch" not in fields:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(wl, n_req: int):
@@ -226,8 +236,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(split_tflops, 1),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(split_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "mla_split_h128" if wl.N % 128 == 0 else "mla_split_h16"
+    roof["traffic"] = measured_traffic(wl)
+    roof["kernel"] = split_kernel_name(wl)
     roof["kernel_ms"] = round(split_ms, 5)
 
     cpu = cpu_baseline(wl, args.cpu_requests) if args.cpu_requests > 0 else None
