@@ -71,9 +71,12 @@ def algorithmic_flops(wl) -> int:
 
 def split_kernel_name(wl) -> str:
     """Symbol prefix of the split kernel the library launches for this shape:
-    the 64-head workgroup kernel when N is a multiple of 64, else the 16-head
-    one."""
-    return "mla_split_wide" if wl.N % 64 == 0 else "mla_split_h16"
+    bf16 cache: the role-split 64-head kernel when N is a multiple of 64;
+    fp8 cache: the wide kernel (128 or 64 heads per workgroup); otherwise the
+    16-head kernel."""
+    if wl.N % 64 == 0:
+        return "mla_split_wide" if wl.cache_dtype == "fp8_e4m3fn" else "mla_split_ws"
+    return "mla_split_h16"
 
 
 def source_hash() -> str:

@@ -694,6 +694,395 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
 }
 
 // ===========================================================================
+// Role-split kernel (bf16 cache, N a multiple of 64): 64 heads per
+// workgroup, 8 waves, two per SIMD.
+//   score waves 0..3: wave q scores heads 16q .. 16q+15 (QK^T on
+//     v_mfma_f32_16x16x32_bf16 as S^T = K . Q^T, 72 VGPRs of query) and runs
+//     the online softmax; it writes bf16 probabilities P[head][token] and the
+//     rescale factor of each head to LDS.
+//   value waves 4..7: wave v accumulates all 64 heads over output columns
+//     128v .. 128v+127 (O^T = V^T . P^T on v_mfma_f32_32x32x16_bf16, 128
+//     accumulator registers), reading V^T from the same LDS tile with
+//     ds_read_b64_tr_b16.
+// Iteration i of the main loop holds one barrier; after it the score waves
+// work on tile i while the value waves work on tile i-1, so on every SIMD the
+// softmax and LDS traffic of one wave overlap the MFMAs of the other.  Tiles
+// are 32 tokens in a 4-stage LDS ring filled by direct-to-LDS loads two tiles
+// ahead (stage (i+2)%4 was last read by the value waves in iteration i-1).
+// ===========================================================================
+constexpr int kWsStages = 4;
+constexpr int kWsPbufBytes = 64 * kPbufRow;                      // P of one tile
+constexpr int kWsPbuf = kWsStages * kStage32;                    // 2 P buffers
+constexpr int kWsAbuf = kWsPbuf + 2 * kWsPbufBytes;              // alpha [2][64]
+constexpr int kWsMbuf = kWsAbuf + 2 * 64 * 4;                    // m [64], l [64]
+constexpr int kWsLds = kWsMbuf + 2 * 64 * 4;
+static_assert(kWsLds <= 160 * 1024, "LDS budget");
+
+// Tile loads are issued by the 4 value waves only: value wave v issues
+// instructions i = v + 4m (m < 9) of the 36 that fill a 32-token tile.
+struct WsDma {
+    static constexpr int kWaves = 4;
+    static constexpr int kDmaLo = 9;
+    static constexpr int kDmaHiWaves = 0;
+};
+
+// One direct-to-LDS load with a wave-uniform 64-bit base in SGPRs and a
+// 32-bit per-lane byte offset (the saddr form: no per-lane 64-bit address
+// arithmetic).
+__device__ __forceinline__ void dma16s(const uint8_t *sbase, int voff, LDS_AS void *dst)
+{
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+// Per-lane source offsets of value wave v's 9 load instructions, relative to
+// the first row of the instruction's half-tile; they do not depend on the
+// tile.  Instruction i fills LDS chunks [64i, 64i+64): chunk q = 64i + lane
+// is row r = q / 72, stored position q % 72, which holds logical chunk
+// (q % 72) ^ swz(r) of the row.
+__device__ __forceinline__ void ws_load_offsets(int v, int lane, int (&off)[9])
+{
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        const int q = i * 64 + lane;
+        const int r = q / kRowChunks;
+        const int c = (q % kRowChunks) ^ swz(r);
+        off[m] = (r - 16 * (i / 18)) * kRowBytes + c * 16;
+    }
+}
+
+// A whole tile (tile_start + 32 <= t_end): two scalar half-tile bases, then
+// 9 loads with the precomputed offsets.
+__device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
+                                              LDS_AS uint8_t *stage, int v, int lane, int b,
+                                              int tile_start, const int (&off)[9])
+{
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int first = tile_start + 16 * h;
+        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
+        base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes;
+    }
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        dma16s(i < 18 ? base[0] : base[1], off[m], stage + i * 1024);
+    }
+}
+
+// Scores of one 32-token tile for a score wave's 16 heads, lazy online
+// softmax, probabilities and rescale factor to LDS.
+template <bool kMask>
+__device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (&qf)[18],
+                                              const LDS_AS uint8_t *stage, LDS_AS uint8_t *prow,
+                                              LDS_AS float *arow, const int (&ko)[2], int g4,
+                                              float scale_log2, int tile_start, int t_end)
+{
+    constexpr int kAhead = 8;
+    auto kfrag = [&](int j) {
+        const int k = j >> 1, tb = j & 1;
+        return *(const LDS_AS bf16x8 *)(stage + ko[k & 1] + (k >> 1) * 128 +
+                                        tb * 16 * kRowBytes);
+    };
+    f32x4 sc4[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    bf16x8 kb[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+        kb[j] = kfrag(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int j = 0; j < 36; ++j) {
+        const bf16x8 a = kb[j % kAhead];
+        if (j + kAhead < 36)
+            kb[j % kAhead] = kfrag(j + kAhead);
+        sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j >> 1], sc4[j & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j + kAhead < 36)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    const f32x4 sc[2] = {sc4[0] + sc4[2], sc4[1] + sc4[3]};
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = sc[tb][i] * scale_log2;
+            if (kMask) {
+                const int tok = tile_start + 16 * tb + 4 * g4 + i;
+                x[4 * tb + i] = tok < t_end ? v : -INFINITY;
+            } else {
+                x[4 * tb + i] = v;
+            }
+            mx = fmaxf(mx, x[4 * tb + i]);
+        }
+    float alpha = 1.0f;
+    if (wave_any(mx > m + kLazyRescale)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m, mx);
+        alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const bf16x2 p01 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb] - m),
+                                     __builtin_amdgcn_exp2f(x[4 * tb + 1] - m));
+        const bf16x2 p23 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb + 2] - m),
+                                     __builtin_amdgcn_exp2f(x[4 * tb + 3] - m));
+        lsum += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+        *(LDS_AS bf16x4 *)(prow + (16 * tb + 4 * g4) * 2) = bf16x4{p01[0], p01[1], p23[0], p23[1]};
+    }
+    l += lsum;
+    if (g4 == 0)
+        *arow = alpha;
+}
+
+// PV of one 32-token tile for a value wave: O^T[col][head] for its 128
+// columns (4 blocks of 32) and the 64 heads (2 blocks of 32).
+__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], const LDS_AS uint8_t *stage,
+                                              const LDS_AS uint8_t *pbuf, const LDS_AS float *abuf,
+                                              const int (&to)[2][2], int r32, int g2)
+{
+    const float al0 = abuf[r32], al1 = abuf[32 + r32];
+    if (wave_any(al0 != 1.0f || al1 != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            o[cb][0] *= al0;
+            o[cb][1] *= al1;
+        }
+    }
+    bf16x8 pf[2][2];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            pf[hb][kk] = *(const LDS_AS bf16x8 *)(pbuf + (32 * hb + r32) * kPbufRow +
+                                                  (16 * kk + 8 * g2) * 2);
+    // V^T fragment j = cb + 4kk (two transposed reads), used by the MFMAs of
+    // both head blocks; kept kAhead fragments ahead.
+    constexpr int kAhead = 2;
+    auto vfrag = [&](int j) {
+        const int cb = j & 3, kk = j >> 2;
+        const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(stage + to[0][cb & 1] + off));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(stage + to[1][cb & 1] + off));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 vb[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+        vb[j] = vfrag(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * kAhead, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bf16x8 a = vb[j % kAhead];
+        if (j + kAhead < 8)
+            vb[j % kAhead] = vfrag(j + kAhead);
+        const int cb = j & 3, kk = j >> 2;
+        o[cb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0][kk], o[cb][0], 0, 0, 0);
+        o[cb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1][kk], o[cb][1], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (j + kAhead < 8)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+}
+
+template <bool kDirect>
+__global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsLds];
+
+    int b, s, hg;
+    decode_work(p, b, s, hg);
+    int t_begin, t_end;
+    chunk_range(p, b, s, t_begin, t_end);
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long head0 = (long long)b * p.N + hg * 64;
+
+    if (t_begin >= t_end) {
+        // empty split: each thread clears 64 columns of one head
+        const int hh = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 64;
+        if (kDirect) {
+            __bf16 *o = p.out + (head0 + hh) * kDV + c0;
+            for (int cc = 0; cc < 64; cc += 8)
+                *(bf16x8 *)(o + cc) = bf16x8{};
+            if (p.lse && (threadIdx.x & 7) == 0)
+                p.lse[head0 + hh] = -INFINITY;
+        } else {
+            float *o = p.part_out + ((head0 + hh) * p.S + s) * kDV + c0;
+            for (int cc = 0; cc < 64; cc += 4)
+                *(f32x4 *)(o + cc) = f32x4{};
+            if ((threadIdx.x & 7) == 0)
+                p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
+        }
+        return;
+    }
+
+    LDS_AS uint8_t *lds = AS3(smem);
+    LDS_AS uint8_t *pbuf = lds + kWsPbuf;
+    LDS_AS float *abuf = (LDS_AS float *)(lds + kWsAbuf);
+    LDS_AS float *mbuf = (LDS_AS float *)(lds + kWsMbuf);
+
+    const int ntiles = (t_end - t_begin + kT32 - 1) / kT32;
+    // Each role runs its own copy of the loop (same barriers), so the query
+    // registers of the score waves and the accumulators of the value waves
+    // are never live at the same time.  Iteration i: after the barrier the
+    // loads of tile i are visible (each value wave waited for its own), the
+    // value waves are done with tile i-2 (stage (i+2)%4) and with P buffer
+    // i%2, and the score waves' P and alpha of tile i-1 are visible.
+    if (w < 4) {
+        // ---- score wave sq: heads 16sq + r16.  Query fragments qf[k] =
+        // q[head][32k + 8 g4 .. +8] (B operand of QK).
+        const int r16 = lane & 15, g4 = lane >> 4;
+        const int sq = w;
+        bf16x8 qf[18];
+        const __bf16 *qp = p.q + (head0 + 16 * sq + r16) * kD + g4 * 8;
+#pragma unroll
+        for (int k = 0; k < 18; ++k)
+            qf[k] = *(const bf16x8 *)(qp + 32 * k);
+        int ko[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
+        LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * kPbufRow;
+        LDS_AS float *arow = abuf + 16 * sq + r16;
+        float m = -INFINITY, l = 0.f;
+        for (int i = 0; i <= ntiles; ++i) {
+            barrier_no_fence();
+            if (i < ntiles) {
+                const int ts = t_begin + i * kT32;
+                if (ts + kT32 <= t_end)
+                    ws_score_tile<false>(m, l, qf, lds + (i & 3) * kStage32,
+                                         prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
+                                         g4, p.scale_log2, ts, t_end);
+                else
+                    ws_score_tile<true>(m, l, qf, lds + (i & 3) * kStage32,
+                                        prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
+                                        g4, p.scale_log2, ts, t_end);
+            }
+            if (i == ntiles - 1) {
+                // final (m, l) of the wave's heads, read by the value waves
+                // after the next barrier
+                float lt = l + __shfl_xor(l, 16);
+                lt += __shfl_xor(lt, 32);
+                if (g4 == 0) {
+                    mbuf[16 * sq + r16] = m;
+                    mbuf[64 + 16 * sq + r16] = lt;
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- value wave vq: columns 128vq .. +128 of all 64 heads; it also
+    // issues its share of every tile's loads, two tiles ahead.
+    // Transposed-read offsets: 16-lane group G reads token rows
+    // 16kk + 8 g2 + 4h + (j >> 2) of columns 128vq + 32cb + 16(G & 1) + 4(j & 3)
+    // (the A operand of O^T = V^T . P^T).
+    const int r32 = lane & 31, g2 = lane >> 5;
+    const int vq = w - 4;
+    int to[2][2];
+    {
+        const int G = lane >> 4, j = lane & 15;
+        const int cl = 2 * (G & 1) + ((j >> 1) & 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rr = 4 * h + (j >> 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                to[h][e] = (8 * g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 +
+                           8 * (j & 1) + 256 * vq;
+        }
+    }
+    int loff[9];
+    ws_load_offsets(vq, lane, loff);
+    PageWindow win;
+    window_fill(p, win, b, t_begin >> p.page_shift, lane);
+    wait_vmcnt<0>();
+    auto issue = [&](int t) {
+        const int ts = t_begin + t * kT32;
+        LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
+        if (ts + kT32 <= t_end)
+            ws_issue_full(p, win, stage, vq, lane, b, ts, loff);
+        else
+            issue_tile_wide<WsDma>(p, win, stage, vq, lane, b, ts, t_end);
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        if (t < ntiles)
+            issue(t);
+    f32x16 o[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+        o[cb][0] = o[cb][1] = f32x16{};
+    for (int i = 0; i <= ntiles; ++i) {
+        if (i < ntiles)
+            wait_tiles_wide<WsDma>(vq, i + 1 < ntiles ? 1 : 0);
+        barrier_no_fence();
+        if (i + 2 < ntiles)
+            issue(i + 2);
+        if (i > 0) {
+            const int j = i - 1;
+            ws_value_tile(o, lds + (j & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
+                          abuf + (j & 1) * 64, to, r32, g2);
+        }
+    }
+
+    // ---- value-wave epilogue: normalise and write heads 32hb + r32,
+    // columns 128v + 32cb + 8q4 + 4g2 .. +4
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const int hh = 32 * hb + r32;
+        const float mh = mbuf[hh];
+        const float lh = mbuf[64 + hh];
+        const float inv = 1.0f / lh;
+        const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
+        const long long orow = head0 + hh;
+        if (kDirect) {
+            __bf16 *op = p.out + orow * kDV + 128 * vq;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int col = cb * 32 + q4 * 8 + g2 * 4;
+                    const f32x16 &a = o[cb][hb];
+                    const bf16x2 v0 = to_bf16x2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
+                    const bf16x2 v1 = to_bf16x2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
+                    *(bf16x4 *)(op + col) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
+                }
+            if (p.lse && vq == 0 && g2 == 0)
+                p.lse[orow] = lse_nat;
+        } else {
+            float *op = p.part_out + (orow * p.S + s) * kDV + 128 * vq;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int col = cb * 32 + q4 * 8 + g2 * 4;
+                    const f32x16 &a = o[cb][hb];
+                    *(f32x4 *)(op + col) = f32x4{a[4 * q4] * inv, a[4 * q4 + 1] * inv,
+                                                 a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv};
+                }
+            if (vq == 0 && g2 == 0)
+                p.part_lse[orow * p.S + s] = lse_nat;
+        }
+    }
+}
+
+// ===========================================================================
 // 16 heads per workgroup: 4 waves, each with its own token stream (16-token
 // tiles; the WG's j-th tile goes to wave j % 4) and private LDS, merged
 // through LDS at the end.  QK^T on v_mfma_f32_16x16x32_bf16, PV on
@@ -1131,40 +1520,49 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     p.page_shift = log2_int(s->page_size);
     const bool direct = part_out == nullptr;
     const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
-    // Head-group size of the wide kernel: 64 heads (4 waves, one per SIMD)
-    // unless MLA_DECODE_WG_HEADS=128 selects 128 heads (8 waves) for
-    // experiments.  Head counts that are not multiples of 64 use the 16-head
-    // kernel.
-    static const int wg_heads = [] {
-        const char *e = getenv("MLA_DECODE_WG_HEADS");
-        return (e && atoi(e) == 128) ? 128 : 64;
-    }();
-    int kind;   // 0: 16 heads, 1: 64 heads, 2: 128 heads per workgroup
-    if (s->num_heads % 128 == 0 && wg_heads == 128)
-        kind = 2;
-    else if (s->num_heads % 64 == 0)
-        kind = 1;
-    else
-        kind = 0;
-    p.HG = s->num_heads / (kind == 2 ? 128 : kind == 1 ? 64 : 16);
+    // Kernel choice by head count and cache dtype:
+    //   bf16, N % 64 == 0:   role-split kernel, 64 heads per workgroup
+    //   fp8,  N % 128 == 0:  wide kernel, 128 heads per workgroup
+    //   fp8,  N % 64 == 0:   wide kernel, 64 heads per workgroup
+    //   otherwise:           16 heads per workgroup
+    int heads_per_wg = 16;
+    if (!fp8 && s->num_heads % 64 == 0)
+        heads_per_wg = 64;
+    else if (fp8 && s->num_heads % 128 == 0)
+        heads_per_wg = 128;
+    else if (fp8 && s->num_heads % 64 == 0)
+        heads_per_wg = 64;
+    p.HG = s->num_heads / heads_per_wg;
     const long long grid = (long long)s->batch * S * p.HG;
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
-    dim3 g((unsigned)grid), blk(kind == 2 ? 512 : 256);
-#define MLA_LAUNCH(...)                                                                         \
-    do {                                                                                        \
-        if (direct && fp8) hipLaunchKernelGGL((__VA_ARGS__ true, true>), g, blk, 0, stream, p);    \
-        else if (direct) hipLaunchKernelGGL((__VA_ARGS__ true, false>), g, blk, 0, stream, p);     \
-        else if (fp8) hipLaunchKernelGGL((__VA_ARGS__ false, true>), g, blk, 0, stream, p);        \
-        else hipLaunchKernelGGL((__VA_ARGS__ false, false>), g, blk, 0, stream, p);                \
-    } while (0)
-    if (kind == 2)
-        MLA_LAUNCH(mla_split_wide<4,);
-    else if (kind == 1)
-        MLA_LAUNCH(mla_split_wide<2,);
-    else
-        MLA_LAUNCH(mla_split_h16<);
-#undef MLA_LAUNCH
+    const dim3 g((unsigned)grid);
+    if (!fp8 && heads_per_wg == 64) {
+        if (direct)
+            hipLaunchKernelGGL(mla_split_ws<true>, g, dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL(mla_split_ws<false>, g, dim3(512), 0, stream, p);
+    } else if (heads_per_wg == 128) {
+        if (direct)
+            hipLaunchKernelGGL((mla_split_wide<4, true, true>), g, dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((mla_split_wide<4, false, true>), g, dim3(512), 0, stream, p);
+    } else if (heads_per_wg == 64) {
+        if (direct)
+            hipLaunchKernelGGL((mla_split_wide<2, true, true>), g, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((mla_split_wide<2, false, true>), g, dim3(256), 0, stream, p);
+    } else if (fp8) {
+        if (direct)
+            hipLaunchKernelGGL((mla_split_h16<true, true>), g, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((mla_split_h16<false, true>), g, dim3(256), 0, stream, p);
+    } else {
+        if (direct)
+            hipLaunchKernelGGL((mla_split_h16<true, false>), g, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((mla_split_h16<false, false>), g, dim3(256), 0, stream, p);
+    }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
