@@ -1,19 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the MLA decode step on one MI355X.
 
-A step is one mla_decode call (split kernel + LSE-merge kernel) over one
-batch of the DeepSeek-V3-shaped decode workload: B = 64 requests, N = 128
-heads, 4096 cached tokens each, page size 64, bf16 query and cache,
-num_kv_splits = 2 (other shapes via --workload).  Inputs are synthetic (seeded), generated on the host and
-resident in HBM before the timed region; three copies of the query, cache
-and page table are rotated so that no step finds its KV rows in the 256 MB
-Infinity Cache left behind by the previous step.
+A step is one mla_decode call over one batch of the DeepSeek-V3-shaped
+decode workload: B = 64 requests, N = 128 heads, 4096 cached tokens each,
+page size 64, bf16 query and cache, num_kv_splits = 2 (other shapes via
+--workload).  The call runs the split-KV attention kernel, then the LSE
+merge kernel (one kernel when num_kv_splits == 1).  Inputs are synthetic (seeded),
+generated on the host and resident in HBM before the timed region; three
+copies of the query, cache and page table are rotated so that no step finds
+its KV rows in the 256 MB Infinity Cache left behind by the previous step.
 
 Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
 (GB/s: every KV row read once, plus q, out, lse, page-table entries and
 lengths), per-step time, TFLOP/s, the split kernel's roofline fraction
-(its duration measured with HIP events on its own stream during the timed
-steps) and the fp64 CPU oracle timed on a sample of the same workload.
+(its duration measured with HIP events on its stream around every timed
+split launch) and the fp64 CPU oracle timed on a sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -54,6 +56,10 @@ def algorithmic_bytes(wl) -> int:
     return kv + wl.B * per_req + 4 * pages + (4 if esz == 1 else 0)
 
 
+def algorithmic_flops(wl) -> int:
+    return 2 * (W.HEAD_SIZE + W.KV_LORA_RANK) * wl.N * wl.total_tokens()
+
+
 def split_kernel_bytes(wl) -> int:
     """Algorithmic bytes of the split kernel alone: KV rows, q, page-table
     entries and lengths (its outputs are the partials, which are not
@@ -65,15 +71,11 @@ def split_kernel_bytes(wl) -> int:
             + 4 * pages)
 
 
-def algorithmic_flops(wl) -> int:
-    return 2 * (W.HEAD_SIZE + W.KV_LORA_RANK) * wl.N * wl.total_tokens()
-
-
 def split_kernel_name(wl) -> str:
-    """Symbol prefix of the split kernel the library launches for this shape:
-    bf16 cache: the role-split 64-head kernel when N is a multiple of 64;
-    fp8 cache: the wide kernel (128 or 64 heads per workgroup); otherwise the
-    16-head kernel."""
+    """Symbol prefix of the split kernel (the dominant one) the library
+    launches for this workload: bf16 cache with N a multiple of 64: the
+    role-split kernel; fp8 cache: the wide kernel; otherwise the 16-head
+    kernel."""
     if wl.N % 64 == 0:
         return "mla_split_wide" if wl.cache_dtype == "fp8_e4m3fn" else "mla_split_ws"
     return "mla_split_h16"
@@ -159,8 +161,8 @@ class Step:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="dsv3", choices=sorted(W.CONFIGS))
     ap.add_argument("--splits", type=int, default=None, help="override num_kv_splits")
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
@@ -201,6 +203,8 @@ def main():
         copies.append(Step(lib, d, wl, S, stream.cuda_stream))
     torch.cuda.synchronize()
 
+    # untimed warmup, long enough for the GPU clocks to reach their steady
+    # state under this load
     for i in range(args.warmup):
         st = copies[i % len(copies)]
         st.split()
@@ -222,23 +226,25 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / K
+    # event time of the split kernel alone, on its stream, every timed step
     split_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    split_gbs = split_kernel_bytes(wl) / (split_ms * 1e-3) / 1e9
-    split_tflops = flops / (split_ms * 1e-3) / 1e12
+    split_bytes = split_kernel_bytes(wl)
+    call_gbs = split_bytes / (split_ms * 1e-3) / 1e9
+    call_tflops = flops / (split_ms * 1e-3) / 1e12
     # The split kernel is bound by HBM when its arithmetic intensity is below
     # the bf16 ridge (312.5 flop/B), as for every bf16 workload here.
-    ai = flops / split_kernel_bytes(wl)
+    ai = flops / split_bytes
     ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4)}
+        roof = {"bound": "hbm", "achieved": round(call_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(call_gbs / HBM_PEAK_GBS, 4)}
     else:
-        roof = {"bound": "mfma", "achieved": round(split_tflops, 1),
+        roof = {"bound": "mfma", "achieved": round(call_tflops, 1),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(split_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+                "frac": round(call_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     roof["traffic"] = measured_traffic(wl)
     roof["kernel"] = split_kernel_name(wl)
     roof["kernel_ms"] = round(split_ms, 5)

@@ -137,11 +137,21 @@ __device__ __forceinline__ int clamp_block(int blk, int num_blocks)
     return blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
 }
 
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
+// left at their maximum so they are not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Page-table window of one wave: lane i holds the block id of logical page
 // base + i of request b, so a tile's block id is one v_readlane away and the
 // tile loop issues no memory access for the page table.  Pages only move
-// forward within a split, and the window is refilled (a vector load) once
-// every 64 pages; the compiler waits for that load before the readlane.
+// forward within a split, and the window is refilled (a vector load, waited
+// for at once) once every 64 pages.
 struct PageWindow {
     int base;         // first logical page held (wave-uniform)
     int ids;          // this lane's entry
@@ -154,6 +164,11 @@ __device__ __forceinline__ void window_fill(const Params &p, PageWindow &win, in
     int idx = page + lane;
     idx = idx < p.MB ? idx : p.MB - 1;
     win.ids = p.block_table[(long long)b * p.MB + idx];
+    // Wait here, inside the (rare) refill, so that the compiler sees no
+    // pending load where the entry is read: otherwise it waits for every
+    // vector-memory operation in flight, tile loads included, before each
+    // readlane of the window.
+    wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ int window_block(const Params &p, PageWindow &win, int b, int page,
@@ -162,16 +177,6 @@ __device__ __forceinline__ int window_block(const Params &p, PageWindow &win, in
     if (page - win.base >= 64)
         window_fill(p, win, b, page, lane);
     return clamp_block(__builtin_amdgcn_readlane(win.ids, page - win.base), p.num_blocks);
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, the other counters
-// left at their maximum so they are not waited on).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // One direct-to-LDS load: lane i's 16 bytes at `src` land at LDS byte
@@ -711,6 +716,10 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
 // ahead (stage (i+2)%4 was last read by the value waves in iteration i-1).
 // ===========================================================================
 constexpr int kWsStages = 4;
+__device__ __forceinline__ LDS_AS uint8_t *stage_of_ws(LDS_AS uint8_t *lds, int t)
+{
+    return lds + (t & (kWsStages - 1)) * kStage32;
+}
 constexpr int kWsPbufBytes = 64 * kPbufRow;                      // P of one tile
 constexpr int kWsPbuf = kWsStages * kStage32;                    // 2 P buffers
 constexpr int kWsAbuf = kWsPbuf + 2 * kWsPbufBytes;              // alpha [2][64]
@@ -831,14 +840,18 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
         m = mnew;
         l *= alpha;
     }
+    // The row sum takes the fp32 probabilities, the MFMA their bf16
+    // roundings: the LSE stays accurate to fp32 whatever the running maximum.
     float lsum = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-        const bf16x2 p01 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb] - m),
-                                     __builtin_amdgcn_exp2f(x[4 * tb + 1] - m));
-        const bf16x2 p23 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb + 2] - m),
-                                     __builtin_amdgcn_exp2f(x[4 * tb + 3] - m));
-        lsum += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            e[j] = __builtin_amdgcn_exp2f(x[4 * tb + j] - m);
+        lsum += (e[0] + e[1]) + (e[2] + e[3]);
+        const bf16x2 p01 = to_bf16x2(e[0], e[1]);
+        const bf16x2 p23 = to_bf16x2(e[2], e[3]);
         *(LDS_AS bf16x4 *)(prow + (16 * tb + 4 * g4) * 2) = bf16x4{p01[0], p01[1], p23[0], p23[1]};
     }
     l += lsum;
@@ -1041,44 +1054,65 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         }
     }
 
-    // ---- value-wave epilogue: normalise and write heads 32hb + r32,
-    // columns 128v + 32cb + 8q4 + 4g2 .. +4
+    // ---- value-wave epilogue.  The accumulator layout scatters a store
+    // instruction over 32 head rows, so the normalised output goes through a
+    // wave-private LDS region first, one head block (32 heads x 128 columns)
+    // at a time, and leaves as whole row segments: 128 columns of one head,
+    // 512 contiguous bytes (fp32 partial) or 256 (bf16 output).  After the
+    // last barrier the value waves read only stage (ntiles-1)%4 and no load
+    // is in flight, so stages ntiles%4 and (ntiles+1)%4 are free: waves 0, 1
+    // take the first, waves 2, 3 the second.  Rows are padded to 528 bytes so
+    // the column-block writes spread over the banks.
+    constexpr int kXRow = 528;
+    LDS_AS uint8_t *xr = stage_of_ws(lds, ntiles + (vq >> 1)) + (vq & 1) * 32 * kXRow;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const int hh = 32 * hb + r32;
         const float mh = mbuf[hh];
         const float lh = mbuf[64 + hh];
         const float inv = 1.0f / lh;
+        // lane (r32, g2) holds head hh, columns 32cb + 8q4 + 4g2 .. +4
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16 &a = o[cb][hb];
+                *(LDS_AS f32x4 *)(xr + r32 * kXRow + (cb * 32 + q4 * 8 + g2 * 4) * 4) =
+                    f32x4{a[4 * q4] * inv, a[4 * q4 + 1] * inv, a[4 * q4 + 2] * inv,
+                          a[4 * q4 + 3] * inv};
+            }
         const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
-        const long long orow = head0 + hh;
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the region is written
         if (kDirect) {
-            __bf16 *op = p.out + orow * kDV + 128 * vq;
+            // 4 heads per instruction: lane l reads head 4it + (l >> 4),
+            // columns 8 (l & 15) .. +8
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int col = cb * 32 + q4 * 8 + g2 * 4;
-                    const f32x16 &a = o[cb][hb];
-                    const bf16x2 v0 = to_bf16x2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
-                    const bf16x2 v1 = to_bf16x2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
-                    *(bf16x4 *)(op + col) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
-                }
+            for (int it = 0; it < 8; ++it) {
+                const int h = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+                const f32x4 v0 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
+                const f32x4 v1 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4 + 16);
+                const bf16x2 a0 = to_bf16x2(v0[0], v0[1]), a1 = to_bf16x2(v0[2], v0[3]);
+                const bf16x2 a2 = to_bf16x2(v1[0], v1[1]), a3 = to_bf16x2(v1[2], v1[3]);
+                *(bf16x8 *)(p.out + (head0 + 32 * hb + h) * kDV + 128 * vq + c) =
+                    bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+            }
             if (p.lse && vq == 0 && g2 == 0)
-                p.lse[orow] = lse_nat;
+                p.lse[head0 + hh] = lse_nat;
         } else {
-            float *op = p.part_out + (orow * p.S + s) * kDV + 128 * vq;
+            // 2 heads per instruction: lane l reads head 2it + (l >> 5),
+            // columns 4 (l & 31) .. +4
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int col = cb * 32 + q4 * 8 + g2 * 4;
-                    const f32x16 &a = o[cb][hb];
-                    *(f32x4 *)(op + col) = f32x4{a[4 * q4] * inv, a[4 * q4 + 1] * inv,
-                                                 a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv};
-                }
+            for (int it = 0; it < 16; ++it) {
+                const int h = 2 * it + (lane >> 5), c = 4 * (lane & 31);
+                *(f32x4 *)(p.part_out + ((head0 + 32 * hb + h) * p.S + s) * kDV + 128 * vq + c) =
+                    *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
+            }
             if (vq == 0 && g2 == 0)
-                p.part_lse[orow * p.S + s] = lse_nat;
+                p.part_lse[(head0 + hh) * p.S + s] = lse_nat;
         }
+        // the reads of this head block are done before the next one
+        // overwrites the region
+        __builtin_amdgcn_s_waitcnt(0xC07F);
     }
 }
 
