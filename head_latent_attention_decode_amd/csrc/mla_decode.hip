@@ -49,6 +49,10 @@ constexpr int kDV = 512;                // value / output width (Lkv)
 constexpr int kRowBytes = kD * 2;       // a bf16 row
 constexpr int kRowChunks = kRowBytes / 16;
 constexpr int kSplitUnit = 32;          // split boundaries are multiples of this
+// Chunks are at least this long, so a short request fills only the first
+// splits and the trailing ones are empty: a chunk's fixed costs (query load,
+// partial write, its share of the merge) stay small next to its KV rows.
+constexpr int kMinChunk = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;    // log2 headroom before a rescale
@@ -118,14 +122,16 @@ __device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int
 }
 
 // Token range [t0, t1) of split s of request b.  The chunk length is
-// ceil(L / S) rounded up to kSplitUnit, a function of (L, S) only.
+// ceil(L / S) rounded up to kSplitUnit and to at least kMinChunk, a function
+// of (L, S) only.
 __device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &t0, int &t1)
 {
     const long long cap = (long long)p.MB << p.page_shift;
     long long L = load_uniform(p.seq_lens, b);
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const long long per = (L + p.S - 1) / p.S;
-    const long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
+    long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
+    C = C > kMinChunk ? C : kMinChunk;
     const long long a = (long long)s * C;
     const long long e = a + C;
     t0 = (int)(a < L ? a : L);
@@ -529,7 +535,8 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
     const long long orow = head0 + 32 * g + ln.r32;               // PV head
 
     if (t_begin >= t_end) {
-        // empty split: (0, -inf), or out = 0 / lse = -inf when direct.
+        // empty split: lse = -inf (its partial output is never read), or out = 0
+        // and lse = -inf when direct.
         // Each thread clears 512 * HB / kThreads = 128 columns of one head.
         const int hh = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 128;
         if (kDirect) {
@@ -538,12 +545,8 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
                 *(bf16x8 *)(o + cc) = bf16x8{};
             if (p.lse && (threadIdx.x & 3) == 0)
                 p.lse[head0 + hh] = -INFINITY;
-        } else {
-            float *o = p.part_out + ((head0 + hh) * p.S + s) * kDV + c0;
-            for (int cc = 0; cc < 128; cc += 4)
-                *(f32x4 *)(o + cc) = f32x4{};
-            if ((threadIdx.x & 3) == 0)
-                p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
+        } else if ((threadIdx.x & 3) == 0) {
+            p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
         }
         return;
     }
@@ -926,7 +929,8 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     const long long head0 = (long long)b * p.N + hg * 64;
 
     if (t_begin >= t_end) {
-        // empty split: each thread clears 64 columns of one head
+        // empty split: lse = -inf (its partial output is never read), or, when
+        // direct, out = 0 and lse = -inf: each thread clears 64 columns of one head
         const int hh = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 64;
         if (kDirect) {
             __bf16 *o = p.out + (head0 + hh) * kDV + c0;
@@ -934,12 +938,8 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
                 *(bf16x8 *)(o + cc) = bf16x8{};
             if (p.lse && (threadIdx.x & 7) == 0)
                 p.lse[head0 + hh] = -INFINITY;
-        } else {
-            float *o = p.part_out + ((head0 + hh) * p.S + s) * kDV + c0;
-            for (int cc = 0; cc < 64; cc += 4)
-                *(f32x4 *)(o + cc) = f32x4{};
-            if ((threadIdx.x & 7) == 0)
-                p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
+        } else if ((threadIdx.x & 7) == 0) {
+            p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
         }
         return;
     }
@@ -1264,7 +1264,8 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
     const long long row_b0 = (long long)b * p.N + hg * 16;   // first head's row
 
     if (t_begin >= t_end) {
-        // empty split: 16 heads x 512 columns, 256 threads
+        // empty split: lse = -inf (its partial output is never read), or, when
+        // direct, out = 0 and lse = -inf for 16 heads x 512 columns
         const int hh = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * 32;
         if (kDirect) {
             __bf16 *o = p.out + (row_b0 + hh) * kDV + c0;
@@ -1272,12 +1273,8 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
                 *(bf16x8 *)(o + c) = bf16x8{};
             if (p.lse && (threadIdx.x & 15) == 0)
                 p.lse[row_b0 + hh] = -INFINITY;
-        } else {
-            float *o = p.part_out + ((row_b0 + hh) * p.S + s) * kDV + c0;
-            for (int c = 0; c < 32; c += 4)
-                *(f32x4 *)(o + c) = f32x4{};
-            if ((threadIdx.x & 15) == 0)
-                p.part_lse[(row_b0 + hh) * p.S + s] = -INFINITY;
+        } else if ((threadIdx.x & 15) == 0) {
+            p.part_lse[(row_b0 + hh) * p.S + s] = -INFINITY;
         }
         return;
     }
@@ -1448,8 +1445,53 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 }
 
 // ===========================================================================
-// LSE merge: one wave per row, each lane owns 8 of the 512 columns.
+// LSE merge.  A state with lse = -inf carries no weight and its output is
+// not read (an empty chunk leaves it unwritten).
+//   mla_merge: one wave per row, each lane owns 8 of the 512 columns.
+//   mla_merge_wide: one workgroup per row for few rows and many states; its
+//   4 waves take every 4th state (loads batched 4 states deep) and add their
+//   sums through LDS.
 // ===========================================================================
+// Largest state lse of a row and the row's total lse (natural log).
+__device__ __forceinline__ void merge_total(const float *ls, int S, float &M, float &total)
+{
+    M = -INFINITY;
+    for (int s = 0; s < S; ++s)
+        M = fmaxf(M, ls[s]);
+    float Z = 0.f;
+    for (int s = 0; s < S; ++s)
+        Z += __builtin_amdgcn_exp2f((ls[s] - M) * kLog2e);
+    total = M + __builtin_amdgcn_logf(Z) * kLn2;
+}
+
+// Weighted sum of the live states s0, s0 + step, ... of one row over this
+// lane's 8 columns.
+__device__ __forceinline__ void merge_sum(const float *po, const float *ls, int S, int s0,
+                                          int step, float total, f32x4 &acc0, f32x4 &acc1)
+{
+    for (int s = s0; s < S; s += step) {
+        const float l = ls[s];
+        if (l == -INFINITY)
+            continue;
+        const float wgt = __builtin_amdgcn_exp2f((l - total) * kLog2e);
+        const f32x4 v0 = *(const f32x4 *)(po + (long long)s * kDV);
+        const f32x4 v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
+        acc0 += wgt * v0;
+        acc1 += wgt * v1;
+    }
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4 &a, const f32x4 &b)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (__bf16)a[e];
+        r[4 + e] = (__bf16)b[e];
+    }
+    return r;
+}
+
 __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_out,
                                                  const float *__restrict__ part_lse,
                                                  __bf16 *__restrict__ out,
@@ -1460,9 +1502,8 @@ __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_
         return;
     const int lane = threadIdx.x & 63;
     const float *ls = part_lse + (long long)row * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s)
-        M = fmaxf(M, ls[s]);
+    float M, total;
+    merge_total(ls, S, M, total);
     __bf16 *o = out + (long long)row * kDV + lane * 8;
     if (M == -INFINITY) {
         *(bf16x8 *)o = bf16x8{};
@@ -1470,28 +1511,74 @@ __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_
             lse[row] = -INFINITY;
         return;
     }
-    float Z = 0.f;
-    for (int s = 0; s < S; ++s)
-        Z += __builtin_amdgcn_exp2f((ls[s] - M) * kLog2e);
-    const float total = M + __builtin_amdgcn_logf(Z) * kLn2;
     f32x4 acc0 = {}, acc1 = {};
-    const float *po = part_out + (long long)row * S * kDV + lane * 8;
-    for (int s = 0; s < S; ++s) {
-        const float wgt = __builtin_amdgcn_exp2f((ls[s] - total) * kLog2e);
-        const f32x4 v0 = *(const f32x4 *)(po + (long long)s * kDV);
-        const f32x4 v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
-        acc0 += wgt * v0;
-        acc1 += wgt * v1;
-    }
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = (__bf16)acc0[e];
-        r[4 + e] = (__bf16)acc1[e];
-    }
-    *(bf16x8 *)o = r;
+    merge_sum(part_out + (long long)row * S * kDV + lane * 8, ls, S, 0, 1, total, acc0, acc1);
+    *(bf16x8 *)o = to_bf16x8(acc0, acc1);
     if (lse && lane == 0)
         lse[row] = total;
+}
+
+__global__ __launch_bounds__(256) void mla_merge_wide(const float *__restrict__ part_out,
+                                                      const float *__restrict__ part_lse,
+                                                      __bf16 *__restrict__ out,
+                                                      float *__restrict__ lse, int rows, int S)
+{
+    __shared__ f32x4 red[3][64][2];
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const float *ls = part_lse + (long long)row * S;
+    float M, total;
+    merge_total(ls, S, M, total);
+    __bf16 *o = out + (long long)row * kDV + lane * 8;
+    if (M == -INFINITY) {
+        if (w == 0) {
+            *(bf16x8 *)o = bf16x8{};
+            if (lse && lane == 0)
+                lse[row] = -INFINITY;
+        }
+        return;
+    }
+    // Every 4th state, 4 at a time with all 8 loads in flight.  A state of
+    // weight zero is loaded too (its workspace row exists) but dropped by a
+    // select, so an unwritten row cannot leak NaN into the sum.
+    f32x4 acc0 = {}, acc1 = {};
+    const float *po = part_out + (long long)row * S * kDV + lane * 8;
+    for (int s0 = w; s0 < S; s0 += 16) {
+        f32x4 v[4][2];
+        float l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + 4 * u < S ? s0 + 4 * u : w;
+            l[u] = s0 + 4 * u < S ? ls[s] : -INFINITY;
+            v[u][0] = *(const f32x4 *)(po + (long long)s * kDV);
+            v[u][1] = *(const f32x4 *)(po + (long long)s * kDV + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool live = l[u] != -INFINITY;
+            const float wgt = __builtin_amdgcn_exp2f((l[u] - total) * kLog2e);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc0[e] += live ? wgt * v[u][0][e] : 0.f;
+                acc1[e] += live ? wgt * v[u][1][e] : 0.f;
+            }
+        }
+    }
+    if (w > 0) {
+        red[w - 1][lane][0] = acc0;
+        red[w - 1][lane][1] = acc1;
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            acc0 += red[k][lane][0];
+            acc1 += red[k][lane][1];
+        }
+        *(bf16x8 *)o = to_bf16x8(acc0, acc1);
+        if (lse && lane == 0)
+            lse[row] = total;
+    }
 }
 
 // ===========================================================================
@@ -1605,9 +1692,16 @@ mla_status_t launch_merge(int rows, int S, const float *part_out, const float *p
 {
     if (rows == 0)
         return MLA_OK;
-    dim3 g((unsigned)((rows + 3) / 4)), blk(256);
-    hipLaunchKernelGGL(mla_merge, g, blk, 0, stream, part_out, part_lse, (__bf16 *)out, lse,
-                       rows, S);
+    // one wave per row fills the GPU once there are a few thousand rows;
+    // below that, and with enough states per row, a workgroup per row
+    if (rows < 4096 && S >= 8) {
+        hipLaunchKernelGGL(mla_merge_wide, dim3((unsigned)rows), dim3(256), 0, stream, part_out,
+                           part_lse, (__bf16 *)out, lse, rows, S);
+    } else {
+        dim3 g((unsigned)((rows + 3) / 4)), blk(256);
+        hipLaunchKernelGGL(mla_merge, g, blk, 0, stream, part_out, part_lse, (__bf16 *)out, lse,
+                           rows, S);
+    }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -173,7 +173,9 @@ def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_spl
 
 def mla_decode_partials(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
                         cache_scale=None, cache_dtype=None, workspace=None):
-    """The split stage alone: returns (part_out f32 [B, N, S, 512], part_lse f32 [B, N, S])."""
+    """The split stage alone: returns (part_out f32 [B, N, S, 512], part_lse f32 [B, N, S]).
+
+    An empty chunk has part_lse = -inf and unwritten part_out rows."""
     _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale)
     shape = make_shape(q, latent_cache, block_table, cache_dtype)
     B, N, S = shape.batch, shape.num_heads, int(num_kv_splits)

@@ -32,8 +32,10 @@
  * count ... kept fixed by default for reproducibility across batch shapes and
  * devices", Model-Optimizer docs, mla_attention_decode, "Parameters").
  * Chunk s of a request of length L covers tokens
- *     [s*C, min((s+1)*C, L)),  C = 32 * ceil(ceil(L / num_kv_splits) / 32);
- * trailing chunks may be empty.
+ *     [s*C, min((s+1)*C, L)),
+ *     C = max(32 * ceil(ceil(L / num_kv_splits) / 32), 1024);
+ * trailing chunks may be empty (a request shorter than 1024 * S fills only
+ * its first ceil(L / C) chunks, so no chunk is dominated by fixed costs).
  *
  * Memory and threading contract, for every entry point:
  *   - Pointers marked "device" point to device memory allocated by the
@@ -149,7 +151,9 @@ mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q,
  * The split stage of mla_decode alone: writes the per-chunk partial states
  *   part_out  = workspace as float [B, N, S, 512] (normalised chunk outputs)
  *   part_lse  = workspace + B*N*S*512 floats, float [B, N, S] (natural log)
- * with (0, -inf) for an empty chunk.  Same arguments and checks as
+ * with lse = -inf for an empty chunk, whose part_out rows are left
+ * unwritten (the merge never reads a state of weight zero).  Same arguments
+ * and checks as
  * mla_decode; requires num_kv_splits >= 1 and a workspace of
  * B * N * S * 513 * 4 bytes (for S == 1 too).  mla_decode is exactly this
  * followed by mla_merge_states on the same workspace.
@@ -168,7 +172,8 @@ mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
  * here for S states with the decode layout):
  *     lse[r]    = ln sum_s exp(part_lse[r, s])
  *     out[r, l] = sum_s exp(part_lse[r, s] - lse[r]) * part_out[r, s, l]
- * A state with lse = -inf carries no weight; a row whose states are all
+ * A state with lse = -inf carries no weight and its part_out row is not
+ * read (it may hold anything, NaN included); a row whose states are all
  * -inf gives out = 0 and lse = -inf.
  *
  *   rows      number of rows R = B * N (>= 0).

@@ -136,8 +136,9 @@ def test_no_lse_output():
 @pytest.mark.parametrize("N,S", [(16, 3), (128, 5)])
 def test_partials_match_oracle_spans(N, S):
     """The split stage alone against the oracle's attention over each chunk,
-    with chunk s = [s*C, min((s+1)*C, L)), C = 32*ceil(ceil(L/S)/32)."""
-    lens = [1, 70, 333, 64]
+    with chunk s = [s*C, min((s+1)*C, L)), C = max(32*ceil(ceil(L/S)/32), 1024).
+    An empty chunk has lse = -inf; its output rows are unspecified."""
+    lens = [1, 70, 5500, 64]
     wl = W.make_workload(4, N, 16, lens, seed=900 + N)
     d = G.to_device(wl)
     po, pl = mla.mla_decode_partials(d["q"], d["latent_cache"], d["block_table"], d["seq_lens"],
@@ -146,7 +147,7 @@ def test_partials_match_oracle_spans(N, S):
     po, pl = po.cpu().numpy(), pl.cpu().numpy()
     rb, rn, t0, t1 = [], [], [], []
     for b, L in enumerate(lens):
-        C = 32 * (-(-(-(-L // S)) // 32))
+        C = max(32 * (-(-(-(-L // S)) // 32)), 1024)
         for n in range(N):
             for s in range(S):
                 a = min(s * C, L)
@@ -154,19 +155,26 @@ def test_partials_match_oracle_spans(N, S):
                 rb.append(b); rn.append(n); t0.append(a); t1.append(e)
     ref_o, ref_l = oracle.attend_spans(G.problem(wl), rb, rn, t0, t1)
     span = np.array(t1) - np.array(t0)
-    G.check(po.reshape(-1, 512), pl.reshape(-1), ref_o, ref_l, span, what="partials")
+    po = po.reshape(-1, 512)
+    po[span == 0] = 0.0                      # unspecified for an empty chunk
+    assert (span == 0).any() and (span > 1024).any()
+    G.check(po, pl.reshape(-1), ref_o, ref_l, span, what="partials")
 
 
-def test_merge_kernel_against_oracle():
-    g = torch.Generator().manual_seed(11)
-    R, S = 300, 7
+@pytest.mark.parametrize("R,S", [(300, 7), (300, 9), (64, 64), (5000, 9)])
+def test_merge_kernel_against_oracle(R, S):
+    """One wave per row (few states, or many rows) and one workgroup per row
+    (few rows with many states) against the oracle's merge."""
+    g = torch.Generator().manual_seed(11 + S)
     po = torch.randn(R, S, 512, generator=g)
     pl = torch.randn(R, S, generator=g) * 3
     pl[torch.rand(R, S, generator=g) < 0.3] = -float("inf")
     pl[:5] = -float("inf")                       # rows with no weight at all
+    po[torch.isneginf(pl)] = float("nan")        # never read: weight zero
     out, lse = mla.mla_merge_states(po.cuda(), pl.cuda())
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle.merge_states(po.double().numpy(), pl.double().numpy())
+    ref_o, ref_l = oracle.merge_states(torch.nan_to_num(po).double().numpy(),
+                                       pl.double().numpy())
     out = out.float().cpu().numpy()
     lse = lse.cpu().numpy()
     assert (out[:5] == 0).all() and np.isneginf(lse[:5]).all()
