@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--cpu-requests", type=int, default=8,
                     help="requests in the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--op", default="decode", choices=["decode", "insert"],
+                    help="decode: the attention step (default); insert: the decode step's "
+                         "query concat and cache insert at the workload's B and N")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -188,6 +191,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "insert":
+        run_insert(args)
+        return
 
     wl = W.config_workload(args.workload)
     S = args.splits or wl.num_kv_splits
@@ -277,6 +284,94 @@ def main():
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                    "input_copies_rotated": len(copies)},
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_insert(args):
+    """The decode step's query concat + cache insert (mla_concat_q_insert_cache)
+    for B new tokens of N heads into a cache of the workload's page shape.
+    Algorithmic bytes: the two query halves read and the concatenated query
+    written (T * N * 576 * 2 each), each new row read (576 * 2) and written
+    (576 * esz), the slots (8 each) and, for fp8, the scale (4)."""
+    spec = W.CONFIGS[args.workload]
+    cache_dtype = spec.get("cache_dtype", "bf16")
+    T, N, P = spec["B"], spec["N"], spec["page_size"]
+    nb = max(T, 4096 // P) * 4
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    copies = []
+    for c in range(max(1, args.copies)):
+        x = W.make_insert_inputs(T, N, nb, P, seed=4242 + c, cache_dtype=cache_dtype)
+        d = dict(ql_nope=x.ql_nope.to(dev), q_pe=x.q_pe.to(dev), kv_c=x.kv_c.to(dev),
+                 k_pe=x.k_pe.to(dev), latent_cache=x.cache.to(dev),
+                 slot_mapping=x.slot_mapping.to(dev),
+                 q_out=torch.empty(T, N, W.HEAD_SIZE, dtype=torch.bfloat16, device=dev))
+        if cache_dtype == "fp8_e4m3fn":
+            d["cache_scale_inv"] = torch.tensor([x.cache_scale_inv], dtype=torch.float32,
+                                                device=dev)
+            d["cache_dtype"] = cache_dtype
+        copies.append((x, d))
+
+    def call(d):
+        mla.concat_q_insert_cache(**d)
+
+    for i in range(args.warmup):
+        call(copies[i % len(copies)][1])
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(copies[i % len(copies)][1])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    esz = 1 if cache_dtype == "fp8_e4m3fn" else 2
+    nbytes = T * N * W.HEAD_SIZE * 2 * 2 + T * W.HEAD_SIZE * (2 + esz) + T * 8 + \
+        (4 if esz == 1 else 0)
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_requests > 0:
+        import oracle
+        x = copies[0][0]
+        bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        cache = (bits(x.cache) if esz == 2 else x.cache.numpy()).copy()
+        oracle.load()
+        c0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - c0 < 1.0 or reps == 0:
+            oracle.concat_insert(bits(x.ql_nope), bits(x.q_pe), bits(x.kv_c), bits(x.k_pe),
+                                 x.slot_mapping.numpy(), cache, x.cache_scale_inv)
+            reps += 1
+        cpu_s = (time.perf_counter() - c0) / reps
+        cpu = {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"the whole step ({T} tokens x {N} heads), "
+                                           f"{reps} runs, {cpu_s * 1e3:.2f} ms each"}
+    line = {
+        "metric": "decode-step query concat + cache insert GB/s (% of HBM roofline)",
+        "value": round(nbytes / (wall / K) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 5),
+        "us_per_step": round(wall * 1e6 / K, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if esz == 2 else "bf16 in, fp8_e4m3fn cache",
+        "data": "synthetic",
+        "config": {"workload": f"insert: T={T} new tokens x N={N} heads, page {P}, "
+                               f"{cache_dtype} cache ({args.workload} shapes)",
+                   "tokens": T, "num_heads": N, "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_concat_insert", "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

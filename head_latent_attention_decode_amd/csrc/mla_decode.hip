@@ -1582,6 +1582,66 @@ __global__ __launch_bounds__(256) void mla_merge_wide(const float *__restrict__ 
 }
 
 // ===========================================================================
+// Decode-step query concat and cache insert.  One 16-byte chunk per thread:
+// first the T * N * 72 chunks of the query (64 from ql_nope, 8 from q_pe per
+// (token, head)), then the cache rows: 72 chunks of 8 bf16 each, or for an
+// fp8 cache 36 chunks of 16 codes (32 bytes of bf16 input each).
+// ===========================================================================
+__global__ __launch_bounds__(256) void mla_concat_insert(
+    const __bf16 *__restrict__ ql_nope, const __bf16 *__restrict__ q_pe,
+    const __bf16 *__restrict__ kv_c, const __bf16 *__restrict__ k_pe,
+    const int64_t *__restrict__ slot_mapping, uint8_t *__restrict__ cache,
+    __bf16 *__restrict__ q_out, const float *__restrict__ scale_inv, long long nq, int T,
+    long long rows, int fp8)
+{
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < nq) {
+        const long long tn = i / 72;
+        const int c = (int)(i % 72);
+        const bf16x8 v = c < 64 ? *(const bf16x8 *)(ql_nope + tn * kDV + 8 * c)
+                                : *(const bf16x8 *)(q_pe + tn * (kD - kDV) + 8 * (c - 64));
+        *(bf16x8 *)(q_out + tn * kD + 8 * c) = v;
+        return;
+    }
+    i -= nq;
+    const int per = fp8 ? 36 : 72;
+    if (i >= (long long)T * per)
+        return;
+    const int t = (int)(i / per), c = (int)(i % per);
+    const long long slot = slot_mapping[t];
+    if (slot < 0 || slot >= rows)
+        return;
+    if (!fp8) {
+        const bf16x8 v = c < 64 ? *(const bf16x8 *)(kv_c + (long long)t * kDV + 8 * c)
+                                : *(const bf16x8 *)(k_pe + (long long)t * (kD - kDV) + 8 * (c - 64));
+        *(bf16x8 *)(cache + (slot * kD + 8 * c) * 2) = v;
+        return;
+    }
+    // 16 elements 16c .. 16c+15 of the row, from kv_c (c < 32) or k_pe
+    const __bf16 *src = c < 32 ? kv_c + (long long)t * kDV + 16 * c
+                               : k_pe + (long long)t * (kD - kDV) + 16 * (c - 32);
+    const bf16x8 a = *(const bf16x8 *)src, b = *(const bf16x8 *)(src + 8);
+    const float s = *scale_inv;
+    // fp32 product, then saturation to the largest finite E4M3FN magnitude
+    // (NaN stays NaN), then the hardware's round-to-nearest-even conversion
+    auto q8 = [&](__bf16 x) {
+        const float f = (float)x * s;
+        return f != f ? f : fminf(fmaxf(f, -448.0f), 448.0f);
+    };
+    unsigned w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bf16x8 &h = k < 2 ? a : b;
+        const int o = 4 * (k & 1);
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(q8(h[o]), q8(h[o + 1]), 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(q8(h[o + 2]), q8(h[o + 3]), r, true);
+        w[k] = (unsigned)r;
+    }
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    *(u32x4 *)(cache + slot * kD + 16 * c) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// ===========================================================================
 // host side
 // ===========================================================================
 bool valid_shape(const mla_decode_shape_t *s, mla_status_t *err)
@@ -1820,6 +1880,37 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *
     if (rows > 0 && (!part_out || !part_lse || !out))
         return MLA_ERR_NULL_POINTER;
     return launch_merge(rows, S, part_out, part_lse, out, lse, stream);
+}
+
+mla_status_t mla_concat_q_insert_cache(int32_t num_tokens, int32_t num_heads,
+                                       const void *ql_nope, const void *q_pe, const void *kv_c,
+                                       const void *k_pe, const int64_t *slot_mapping,
+                                       int32_t num_blocks, int32_t page_size,
+                                       mla_cache_dtype_t cache_dtype, const float *cache_scale_inv,
+                                       void *latent_cache, void *q_out, hipStream_t stream)
+{
+    if (num_tokens < 0 || num_heads < 0 || num_blocks < 0 || page_size < 1)
+        return MLA_ERR_BAD_SHAPE;
+    if (cache_dtype != MLA_CACHE_BF16 && cache_dtype != MLA_CACHE_FP8_E4M3FN)
+        return MLA_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == MLA_CACHE_FP8_E4M3FN;
+    if (num_tokens == 0)
+        return MLA_OK;
+    if (!kv_c || !k_pe || !slot_mapping || !latent_cache || (fp8 && !cache_scale_inv))
+        return MLA_ERR_NULL_POINTER;
+    if (num_heads > 0 && (!ql_nope || !q_pe || !q_out))
+        return MLA_ERR_NULL_POINTER;
+    const long long nq = (long long)num_tokens * num_heads * 72;
+    const long long total = nq + (long long)num_tokens * (fp8 ? 36 : 72);
+    const long long blocks = (total + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(mla_concat_insert, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const __bf16 *)ql_nope, (const __bf16 *)q_pe, (const __bf16 *)kv_c,
+                       (const __bf16 *)k_pe, slot_mapping, (uint8_t *)latent_cache,
+                       (__bf16 *)q_out, cache_scale_inv, nq, num_tokens,
+                       (long long)num_blocks * page_size, fp8 ? 1 : 0);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 } // extern "C"

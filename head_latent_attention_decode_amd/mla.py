@@ -31,7 +31,7 @@ HEAD_SIZE = KV_LORA_RANK + QK_ROPE_HEAD_DIM
 MAX_KV_SPLITS = 256
 
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
-            "mla_decode_partials", "mla_merge_states")
+            "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache")
 
 
 class MLAError(RuntimeError):
@@ -74,6 +74,9 @@ def load(path: Path | str | None = None):
                                         ctypes.c_float, i32, vp, sz, vp]
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_concat_q_insert_cache.restype = ctypes.c_int
+    lib.mla_concat_q_insert_cache.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp,
+                                              vp, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -216,3 +219,39 @@ def mla_merge_states(part_out, part_lse, *, out=None, lse=None, return_lse=True)
                                  _ptr(lse), _stream(part_out.device))
     _check(st, "mla_merge_states")
     return out, lse
+
+
+def concat_q_insert_cache(ql_nope, q_pe, kv_c, k_pe, latent_cache, slot_mapping, *,
+                          cache_scale_inv=None, cache_dtype=None, q_out=None):
+    """Decode-step query concat and cache insert (mla_concat_q_insert_cache).
+
+    ql_nope bf16 [T, N, 512], q_pe bf16 [T, N, 64], kv_c bf16 [T, 512],
+    k_pe bf16 [T, 64], slot_mapping int64 [T]; latent_cache [num_blocks,
+    page_size, 576] (bf16, or E4M3FN with cache_scale_inv, a 1-element f32
+    tensor) is updated in place.  Returns q_out bf16 [T, N, 576].
+    """
+    T, N = int(ql_nope.shape[0]), int(ql_nope.shape[1])
+    for name, t, shape in (("ql_nope", ql_nope, (T, N, KV_LORA_RANK)),
+                           ("q_pe", q_pe, (T, N, QK_ROPE_HEAD_DIM)),
+                           ("kv_c", kv_c, (T, KV_LORA_RANK)),
+                           ("k_pe", k_pe, (T, QK_ROPE_HEAD_DIM))):
+        if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if latent_cache.dim() != 3 or latent_cache.shape[2] != HEAD_SIZE or \
+            not latent_cache.is_contiguous():
+        raise ValueError("latent_cache must be a contiguous [num_blocks, page_size, 576] tensor")
+    dt = _cache_dtype(latent_cache, cache_dtype)
+    if dt == MLA_CACHE_FP8_E4M3FN and (cache_scale_inv is None or
+                                       cache_scale_inv.dtype != torch.float32):
+        raise ValueError("an fp8 cache needs cache_scale_inv (float32, one element)")
+    if q_out is None:
+        q_out = torch.empty((T, N, HEAD_SIZE), dtype=torch.bfloat16, device=ql_nope.device)
+    st = load().mla_concat_q_insert_cache(
+        T, N, _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(slot_mapping),
+        int(latent_cache.shape[0]), int(latent_cache.shape[1]), dt,
+        _ptr(cache_scale_inv) if dt == MLA_CACHE_FP8_E4M3FN else None, _ptr(latent_cache),
+        _ptr(q_out), _stream(ql_nope.device))
+    _check(st, "mla_concat_q_insert_cache")
+    return q_out

@@ -232,3 +232,58 @@ def config_workload(name: str, **overrides) -> Workload:
     P = spec.pop("page_size")
     lens = spec.pop("seq_lens")
     return make_workload(B, N, P, lens, name=name, **spec)
+
+
+@dataclass
+class InsertInputs:
+    """One decode step's new-token data and a paged cache to insert it into."""
+    ql_nope: torch.Tensor       # bfloat16 [T, N, 512], CPU
+    q_pe: torch.Tensor          # bfloat16 [T, N, 64], CPU
+    kv_c: torch.Tensor          # bfloat16 [T, 512], CPU
+    k_pe: torch.Tensor          # bfloat16 [T, 64], CPU
+    slot_mapping: torch.Tensor  # int64 [T], CPU; -1 marks a padding token
+    cache: torch.Tensor         # bfloat16 or uint8 [num_blocks, page, 576], CPU
+    cache_scale_inv: float      # a float32 value; 1.0 for bf16
+    cache_dtype: str
+
+
+def make_insert_inputs(T, N, num_blocks, page_size, *, seed, cache_dtype="bf16",
+                       pad_every=0) -> InsertInputs:
+    """Seeded inputs of a decode step's query concat and cache insert.
+
+    Values are float32 N(0, 1) rounded to bfloat16, as for the workloads.  The
+    T slots are distinct rows of the cache drawn by a random permutation;
+    every pad_every-th token (if pad_every > 0) gets slot -1.  The cache starts
+    with random contents: N(0, 1) bf16 values, or random E4M3FN codes other
+    than NaN.  For an fp8 cache the per-tensor scale follows the workloads'
+    convention, amax(|kv_c, k_pe|) / 448, and cache_scale_inv is its float32
+    reciprocal (the caller pre-inverts it).
+    """
+    if cache_dtype not in ("bf16", "fp8_e4m3fn"):
+        raise ValueError(cache_dtype)
+    rows = num_blocks * page_size
+    if T > rows:
+        raise ValueError("more tokens than cache rows")
+    g = torch.Generator().manual_seed(seed)
+    ql_nope = torch.randn(T, N, KV_LORA_RANK, generator=g).to(torch.bfloat16)
+    q_pe = torch.randn(T, N, QK_ROPE_HEAD_DIM, generator=g).to(torch.bfloat16)
+    kv_c = torch.randn(T, KV_LORA_RANK, generator=g).to(torch.bfloat16)
+    k_pe = torch.randn(T, QK_ROPE_HEAD_DIM, generator=g).to(torch.bfloat16)
+    rng = np.random.default_rng(seed + 104729)
+    slots = rng.permutation(rows)[:T].astype(np.int64)
+    if pad_every > 0:
+        slots[::pad_every] = -1
+    if cache_dtype == "bf16":
+        cache = torch.randn(num_blocks, page_size, HEAD_SIZE, generator=g).to(torch.bfloat16)
+        inv = 1.0
+    else:
+        codes = torch.randint(0, 255, (num_blocks, page_size, HEAD_SIZE), generator=g)
+        cache = torch.where(codes >= 0x7F, codes + 1, codes).to(torch.uint8)   # no 0x7F
+        cache[cache == 0xFF] = 0xFE                                              # no 0xFF
+        amax = float(torch.cat([kv_c.float().abs().flatten(), k_pe.float().abs().flatten()]).max()) \
+            if T else 1.0
+        scale = np.float32(np.float32(amax) / np.float32(E4M3_MAX))
+        inv = float(np.float32(1.0) / scale)
+    return InsertInputs(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe,
+                        slot_mapping=torch.from_numpy(slots), cache=cache,
+                        cache_scale_inv=inv, cache_dtype=cache_dtype)

@@ -188,6 +188,48 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
                               const float *part_out, const float *part_lse,
                               void *out, float *lse, hipStream_t stream);
 
+/*
+ * The step before the attention of a decode step: form the absorbed query and
+ * insert the step's new latent row into the paged cache, in one launch
+ * (raon-1-mini mla_attention.py, the model-layer page, decode path of forward
+ * and _decode_concat_cache; vLLM API docs, mla_attention, forward with a
+ * direct call and unified_mla_kv_cache_update: the insert precedes the
+ * attention of the same step, at the slot given by slot_mapping).
+ *     q_out[t, n, :]          = cat[ql_nope[t, n, :], q_pe[t, n, :]]   (512 + 64)
+ *     cache row slot_mapping[t] = cat[kv_c[t, :], k_pe[t, :]]
+ * For an fp8 cache each element is stored as the E4M3FN code nearest to the
+ * fp32 product x * cache_scale_inv (round to nearest even, saturating at
+ * +-448): the pre-inverted per-tensor scale of the model-layer page, so that
+ * a reader multiplying by cache_scale (= 1 / cache_scale_inv) gets x back.
+ *
+ *   num_tokens       T >= 0 new tokens (one per decoding request).
+ *   num_heads        N >= 0; N == 0 inserts without forming a query.
+ *   ql_nope          device, bf16 [T, N, 512] (the absorbed no-rope query).
+ *   q_pe             device, bf16 [T, N, 64].
+ *   kv_c, k_pe       device, bf16 [T, 512] and [T, 64] (the new latent row).
+ *   slot_mapping     device, int64 [T]: flat row block * page_size + row of
+ *                    the [num_blocks, page_size, 576] cache.  A negative
+ *                    slot (a padding token) and a slot >= num_blocks *
+ *                    page_size write nothing.  Slots must be distinct.
+ *   num_blocks, page_size   the cache's shape (page_size >= 1).
+ *   cache_dtype      MLA_CACHE_BF16 or MLA_CACHE_FP8_E4M3FN.
+ *   cache_scale_inv  device, one float (fp8 only; ignored and may be NULL
+ *                    for bf16).
+ *   latent_cache     device, updated in place.
+ *   q_out            device, bf16 [T, N, 576]; may be NULL when N == 0.
+ * Errors: MLA_ERR_BAD_SHAPE for a negative count or page_size < 1,
+ * MLA_ERR_UNSUPPORTED for another cache dtype, MLA_ERR_NULL_POINTER for a
+ * missing required pointer (nothing is launched then).  Asynchronous on
+ * `stream`; the library allocates nothing.
+ */
+mla_status_t mla_concat_q_insert_cache(int32_t num_tokens, int32_t num_heads,
+                                       const void *ql_nope, const void *q_pe,
+                                       const void *kv_c, const void *k_pe,
+                                       const int64_t *slot_mapping, int32_t num_blocks,
+                                       int32_t page_size, mla_cache_dtype_t cache_dtype,
+                                       const float *cache_scale_inv, void *latent_cache,
+                                       void *q_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

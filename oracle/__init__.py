@@ -74,6 +74,11 @@ def _declare(lib):
     lib.oracle_mla_attend_spans.argtypes = common + [i32, P, P, P, P, P, P, i32]
     lib.oracle_merge_states.restype = None
     lib.oracle_merge_states.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_e4m3fn_from_float.restype = ctypes.c_uint8
+    lib.oracle_e4m3fn_from_float.argtypes = [ctypes.c_float]
+    lib.oracle_concat_insert.restype = None
+    lib.oracle_concat_insert.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32, i32, i32,
+                                         ctypes.c_float, P, P]
 
 
 def _ptr(a: np.ndarray):
@@ -186,3 +191,36 @@ def bf16_to_double(bits: int, lib=None) -> float:
 
 def e4m3fn_to_double(bits: int, lib=None) -> float:
     return (lib or load()).oracle_e4m3fn_to_double(bits)
+
+
+def e4m3fn_from_float(value: float, lib=None) -> int:
+    """Nearest OCP E4M3FN code to the fp32 value (ties to even, saturating)."""
+    return int((lib or load()).oracle_e4m3fn_from_float(float(np.float32(value))))
+
+
+def concat_insert(ql_nope, q_pe, kv_c, k_pe, slot_mapping, cache, scale_inv=1.0, lib=None):
+    """The decode step's query concat and cache insert (see mla_oracle.c).
+
+    ql_nope uint16 [T, N, 512], q_pe uint16 [T, N, 64], kv_c uint16 [T, 512],
+    k_pe uint16 [T, 64] (bf16 bits); slot_mapping int64 [T]; cache uint16
+    (bf16 bits) or uint8 (E4M3FN codes) [num_blocks, page_size, 576], updated
+    in place.  Returns q_out uint16 [T, N, 576].
+    """
+    ql_nope = np.ascontiguousarray(ql_nope, dtype=np.uint16)
+    q_pe = np.ascontiguousarray(q_pe, dtype=np.uint16)
+    kv_c = np.ascontiguousarray(kv_c, dtype=np.uint16)
+    k_pe = np.ascontiguousarray(k_pe, dtype=np.uint16)
+    slot = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    if not cache.flags["C_CONTIGUOUS"] or cache.dtype not in (np.uint16, np.uint8):
+        raise TypeError("cache must be a contiguous uint16 or uint8 array")
+    T, N, Dn = ql_nope.shape
+    Dr = q_pe.shape[2]
+    nb, P, D = cache.shape
+    if D != Dn + Dr:
+        raise ValueError("cache width must be Dn + Dr")
+    q_out = np.zeros((T, N, D), dtype=np.uint16)
+    (lib or load()).oracle_concat_insert(
+        T, N, Dn, Dr, _ptr(ql_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe), _ptr(slot), nb, P,
+        1 if cache.dtype == np.uint8 else 0, float(np.float32(scale_inv)), _ptr(cache),
+        _ptr(q_out))
+    return q_out

@@ -359,3 +359,85 @@ void oracle_merge_states(int R, int S, int Dv, const double *part_out,
         }
     }
 }
+
+/* ---- decode-step cache insert and query concat ---------------------------
+ *
+ * raon-1-mini mla_attention.py (the model-layer page), the decode path of
+ * forward and _decode_concat_cache: before the attention of a decode step,
+ * one launch forms the absorbed query as the concatenation [ql_nope, q_pe]
+ * (width 512 + 64) and writes the step's new latent row [kv_c, k_pe] into the
+ * paged cache at its slot.  vLLM API docs, mla_attention (forward with a
+ * direct call, and unified_mla_kv_cache_update): the slot comes from the
+ * forward context's slot_mapping, and the insert happens before the
+ * attention of the same step.  The vLLM MLA common page's
+ * concat_and_cache_mla call writes the same row layout.  For an fp8 cache
+ * the row is stored as value * cache_scale_inv, the pre-inverted scale (the
+ * model-layer page's _k_scale_inv buffer): the stored value times the scale
+ * gives the latent back, as the readers assume.
+ *
+ * Readings (the pages do not spell these out):
+ *   - a slot is block * page_size + row, i.e. the flat row index of the
+ *     [num_blocks, page_size, 576] cache;
+ *   - a negative slot marks a padding token that writes nothing; a slot at or
+ *     beyond num_blocks * page_size is likewise skipped;
+ *   - the fp8 product value * scale_inv is formed in fp32 (where a float
+ *     decides a code, both sides decide in the kernel's precision), then
+ *     rounded to the nearest E4M3FN value with ties to the even code,
+ *     magnitudes beyond 448 saturating to +-448.
+ */
+
+/* Nearest E4M3FN code to a float: magnitudes of 448 and beyond saturate to
+ * the largest finite code; otherwise every finite non-negative code is tried
+ * through the decoder above (pinned on the full code table), ties to the even
+ * code, the sign applied last.  NaN gives the NaN code 0x7F. */
+uint8_t oracle_e4m3fn_from_float(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    const double a = fabs((double)v);
+    if (a >= 448.0)                 /* saturation: the largest finite code */
+        return (uint8_t)(signbit(v) ? 0xFE : 0x7E);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int k = 0; k <= 0x7E; ++k) {
+        const double err = fabs(oracle_e4m3fn_to_double((uint8_t)k) - a);
+        if (err < best_err || (err == best_err && (k & 1) == 0 && (best & 1) == 1)) {
+            best = k;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(signbit(v) ? (best | 0x80) : best);
+}
+
+/* ql_nope [T, N, Dn], q_pe [T, N, Dr], kv_c [T, Dn], k_pe [T, Dr]: bf16 bits.
+ * q_out [T, N, Dn + Dr] bf16 bits.  cache [num_blocks * page_size, Dn + Dr]:
+ * bf16 bits (fp8 == 0) or E4M3FN codes (fp8 == 1). */
+void oracle_concat_insert(int T, int N, int Dn, int Dr, const uint16_t *ql_nope,
+                          const uint16_t *q_pe, const uint16_t *kv_c, const uint16_t *k_pe,
+                          const int64_t *slot_mapping, int num_blocks, int page_size, int fp8,
+                          float scale_inv, void *cache, uint16_t *q_out)
+{
+    const int D = Dn + Dr;
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n)
+            for (int d = 0; d < D; ++d)
+                q_out[((int64_t)t * N + n) * D + d] =
+                    d < Dn ? ql_nope[((int64_t)t * N + n) * Dn + d]
+                           : q_pe[((int64_t)t * N + n) * Dr + (d - Dn)];
+    const int64_t rows = (int64_t)num_blocks * page_size;
+    for (int t = 0; t < T; ++t) {
+        const int64_t s = slot_mapping[t];
+        if (s < 0 || s >= rows)
+            continue;
+        for (int d = 0; d < D; ++d) {
+            const uint16_t bits = d < Dn ? kv_c[(int64_t)t * Dn + d] : k_pe[(int64_t)t * Dr + (d - Dn)];
+            if (!fp8) {
+                ((uint16_t *)cache)[s * D + d] = bits;
+            } else {
+                const float x = (float)oracle_bf16_to_double(bits);
+                const float v = x * scale_inv;
+                ((uint8_t *)cache)[s * D + d] = oracle_e4m3fn_from_float(v);
+            }
+        }
+    }
+}

@@ -106,3 +106,22 @@ def test_partials_arguments(lib):
     shp = shape()
     assert g(ctypes.byref(shp), FAKE, FAKE, None, FAKE, FAKE, 0.1, 4, FAKE, 10, None) == 5
     assert g(ctypes.byref(shp), FAKE, FAKE, None, FAKE, FAKE, 0.1, 0, FAKE, 1 << 30, None) == 4
+
+
+def insert(lib, T=4, N=8, ql=FAKE, qp=FAKE, kv=FAKE, kp=FAKE, slots=FAKE, nb=10, P=64, dt=0,
+           inv=None, cache=FAKE, q_out=FAKE):
+    return lib.mla_concat_q_insert_cache(T, N, ql, qp, kv, kp, slots, nb, P, dt, inv, cache,
+                                         q_out, None)
+
+
+def test_insert_arguments(lib):
+    """Every invalid call returns before a launch (the pointers are fake)."""
+    assert insert(lib, T=-1) == 2 and insert(lib, N=-1) == 2
+    assert insert(lib, nb=-1) == 2 and insert(lib, P=0) == 2
+    assert insert(lib, dt=7) == 3
+    assert insert(lib, T=0) == 0                       # nothing to do
+    assert insert(lib, kv=None) == 1 and insert(lib, kp=None) == 1
+    assert insert(lib, slots=None) == 1 and insert(lib, cache=None) == 1
+    assert insert(lib, dt=1) == 1                      # fp8 needs cache_scale_inv
+    assert insert(lib, ql=None) == 1 and insert(lib, qp=None) == 1
+    assert insert(lib, q_out=None) == 1
