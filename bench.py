@@ -168,9 +168,11 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--cpu-requests", type=int, default=8,
                     help="requests in the CPU-oracle sample (0 disables it)")
-    ap.add_argument("--op", default="decode", choices=["decode", "insert"],
+    ap.add_argument("--op", default="decode", choices=["decode", "insert", "gather", "merge2"],
                     help="decode: the attention step (default); insert: the decode step's "
-                         "query concat and cache insert at the workload's B and N")
+                         "query concat and cache insert at the workload's B and N; gather: "
+                         "the chunked-context gather of the workload's whole context; "
+                         "merge2: the two-state merge of prefill partials")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -194,6 +196,12 @@ def main():
 
     if args.op == "insert":
         run_insert(args)
+        return
+    if args.op == "gather":
+        run_gather(args)
+        return
+    if args.op == "merge2":
+        run_merge2(args)
         return
 
     wl = W.config_workload(args.workload)
@@ -374,6 +382,124 @@ def run_insert(args):
                      "kernel": "mla_concat_insert", "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+
+
+def _time_calls(calls, warmup, steps):
+    """Warm up, then time `steps` calls (rotating over `calls`) with HIP events
+    around each launch on the current stream; returns (mean event ms, wall s)."""
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        calls[i % len(calls)]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
+
+
+def _op_line(metric, nbytes, kernel_ms, wall, steps, warmup, kernel, workload, dtype, cpu,
+             extra=None):
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    cfg = {"workload": workload, "algorithmic_bytes": nbytes}
+    cfg.update(extra or {})
+    return {
+        "metric": metric, "value": round(nbytes / (wall / steps) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 5), "us_per_step": round(wall * 1e6 / steps, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic", "config": cfg,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kernel, "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_gather(args):
+    """The chunked-context gather of the workload's whole context (one chunk
+    covering every request from token 0): each row read once from the paged
+    cache (576 * esz bytes) and written as bf16 (1152 bytes), plus the page
+    table, offsets and row owners."""
+    wl = W.config_workload(args.workload)
+    dev = torch.device("cuda:0")
+    lens = wl.seq_lens.to(torch.int64)
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lens, 0)]).to(torch.int32)
+    tts = torch.repeat_interleave(torch.arange(wl.B, dtype=torch.int32), lens)
+    n = int(lens.sum())
+    fp8 = wl.cache_dtype == "fp8_e4m3fn"
+    cache = wl.cache.to(dev)
+    d = dict(latent_cache=cache, block_table=wl.block_table.to(dev), cu_seq_lens=cu.to(dev),
+             token_to_seq=tts.to(dev),
+             dst=torch.empty(n, W.HEAD_SIZE, dtype=torch.bfloat16, device=dev))
+    if fp8:
+        d.update(cache_scale=torch.tensor([wl.cache_scale], dtype=torch.float32, device=dev),
+                 cache_dtype=wl.cache_dtype)
+    kernel_ms, wall = _time_calls([lambda: mla.gather_cache(**d)], args.warmup, args.steps)
+    esz = 1 if fp8 else 2
+    pages = int(((lens + wl.page_size - 1) // wl.page_size).sum())
+    nbytes = n * W.HEAD_SIZE * (esz + 2) + 4 * pages + 4 * (wl.B + 1) + 4 * n
+    cpu = None
+    if args.cpu_requests > 0:
+        import oracle
+        k = min(args.cpu_requests, wl.B)
+        bits = (lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16))
+        cache_np = bits(wl.cache) if not fp8 else wl.cache.numpy()
+        m = int(cu[k])
+        c0 = time.perf_counter()
+        oracle.gather(cache_np, wl.block_table.numpy()[:k], cu.numpy()[:k + 1],
+                      tts.numpy()[:m], scale=wl.cache_scale)
+        cpu_s = time.perf_counter() - c0
+        sb = m * W.HEAD_SIZE * (esz + 2)
+        cpu = {"value": round(sb / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{k} of {wl.B} requests ({m} rows), {cpu_s:.2f} s"}
+    line = _op_line("chunked-context gather GB/s (% of HBM roofline)", nbytes, kernel_ms, wall,
+                    args.steps, args.warmup, "mla_gather",
+                    f"gather: {wl.name} context, {wl.B} requests, {n} rows, page "
+                    f"{wl.page_size}, {wl.cache_dtype} cache -> bf16 workspace",
+                    "bf16" if not fp8 else "fp8_e4m3fn cache -> bf16", cpu, {"rows": n})
+    print(json.dumps(line), flush=True)
+
+
+def run_merge2(args):
+    """The two-state merge of prefill partials: T = 8192 tokens x N = 128
+    heads x D = 128 (DeepSeek-V3's v_head_dim) bf16 outputs and [N, T] fp32
+    LSEs; both states read, the merged state written."""
+    T, N, D = 8192, 128, 128
+    dev = torch.device("cuda:0")
+    copies = []
+    for c in range(max(1, args.copies)):
+        m = W.make_merge_inputs(T, N, D, seed=600 + c)
+        dd = dict(prefix_out=m.prefix_out.to(dev), prefix_lse=m.prefix_lse.to(dev),
+                  suffix_out=m.suffix_out.to(dev), suffix_lse=m.suffix_lse.to(dev))
+        dd["out"] = torch.empty_like(dd["prefix_out"])
+        dd["out_lse"] = torch.empty_like(dd["prefix_lse"])
+        copies.append((m, dd))
+    calls = [(lambda dd=dd: mla.merge_attn_states(**dd)) for _, dd in copies]
+    kernel_ms, wall = _time_calls(calls, args.warmup, args.steps)
+    nbytes = 3 * T * N * D * 2 + 3 * N * T * 4
+    cpu = None
+    if args.cpu_requests > 0:
+        import oracle
+        m = copies[0][0]
+        k = 256
+        c0 = time.perf_counter()
+        oracle.merge_two(m.prefix_out[:k].double().numpy(), m.prefix_lse[:, :k].double().numpy(),
+                         m.suffix_out[:k].double().numpy(), m.suffix_lse[:, :k].double().numpy())
+        cpu_s = time.perf_counter() - c0
+        sb = 3 * k * N * D * 2 + 3 * N * k * 4
+        cpu = {"value": round(sb / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{k} of {T} tokens, all heads, {cpu_s:.2f} s"}
+    line = _op_line("two-state LSE merge GB/s (% of HBM roofline)", nbytes, kernel_ms, wall,
+                    args.steps, args.warmup, "mla_merge_two",
+                    f"merge2: T={T} tokens x N={N} heads x D={D}, bf16 states, [N, T] lse",
+                    "bf16 states, fp32 lse", cpu)
     print(json.dumps(line), flush=True)
 
 

@@ -1642,6 +1642,129 @@ __global__ __launch_bounds__(256) void mla_concat_insert(
 }
 
 // ===========================================================================
+// Chunked-context gather: 18 threads per workspace row, each doing the row's
+// index chain once (owner, start, page, block) and then moving 4 of its 72
+// 16-byte bf16 chunks, or converting 2 of its 36 16-code fp8 chunks (16 codes
+// in, 16 bf16 out).  Workspace row i belongs to request token_to_seq[i] and
+// holds its token seq_starts[b] + i - cu_seq_lens[b]; indices are clamped so
+// that every read stays inside the table and the cache whatever they hold.
+// ===========================================================================
+__global__ __launch_bounds__(256) void mla_gather(
+    const uint8_t *__restrict__ cache, int fp8, const float *__restrict__ scale,
+    const int32_t *__restrict__ block_table, int B, int MB, int num_blocks, int page_size,
+    const int32_t *__restrict__ cu_seq_lens, const int32_t *__restrict__ token_to_seq,
+    const int32_t *__restrict__ seq_starts, __bf16 *__restrict__ dst, long long n_threads)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_threads)
+        return;
+    const long long tok = i / 18;
+    const int k = (int)(i % 18);
+    int b = token_to_seq[tok];
+    b = b < 0 ? 0 : (b >= B ? B - 1 : b);
+    long long pos = (long long)(seq_starts ? seq_starts[b] : 0) + (tok - cu_seq_lens[b]);
+    pos = pos < 0 ? 0 : pos;
+    long long pg = pos / page_size;
+    pg = pg >= MB ? MB - 1 : pg;
+    const int blk = clamp_block(block_table[(long long)b * MB + pg], num_blocks);
+    const long long row = (long long)blk * page_size + pos % page_size;
+    __bf16 *d = dst + tok * kD;
+    if (!fp8) {
+        const bf16x8 *src = (const bf16x8 *)(cache + row * kD * 2);
+        bf16x8 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = src[k + 18 * j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(bf16x8 *)(d + 8 * (k + 18 * j)) = v[j];
+        return;
+    }
+    // 16 codes at a time, decoded exactly to fp32, times the scale in fp32,
+    // rounded to bf16 (nearest even)
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 *src = (const u32x4 *)(cache + row * kD);
+    const float sc = *scale;
+    u32x4 v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        v[j] = src[k + 18 * j];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        bf16x8 r[2];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[j][w], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[j][w], true);
+            const bf16x2 a = to_bf16x2(lo[0] * sc, lo[1] * sc);
+            const bf16x2 c = to_bf16x2(hi[0] * sc, hi[1] * sc);
+            bf16x8 &o = r[w >> 1];
+            const int e = 4 * (w & 1);
+            o[e] = a[0];
+            o[e + 1] = a[1];
+            o[e + 2] = c[0];
+            o[e + 3] = c[1];
+        }
+        *(bf16x8 *)(d + 16 * (k + 18 * j)) = r[0];
+        *(bf16x8 *)(d + 16 * (k + 18 * j) + 8) = r[1];
+    }
+}
+
+// ===========================================================================
+// Two-state merge (the prefill context accumulation): per (token, head) the
+// prefix and suffix states combine as out = (wp * p + ws * s) / (wp + ws),
+// lse = M + ln(wp + ws), w = e^(lse - M), M the larger lse; two states of
+// weight zero give (0, -inf).  One 8-element chunk per thread; the
+// D / 8 chunks of a row share a workgroup, so the lse, which may be written
+// over its own input, is stored after a workgroup barrier.
+// ===========================================================================
+__global__ __launch_bounds__(256) void mla_merge_two(
+    const __bf16 *prefix_out, const float *prefix_lse, const __bf16 *suffix_out,
+    const float *suffix_lse, __bf16 *out, float *out_lse, int T, int N, int D, long long n_chunks)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int cpr = D / 8;
+    const bool live = i < n_chunks;
+    const long long rowi = live ? i / cpr : 0;
+    const int c = (int)(i % cpr);
+    const long long t = rowi / N, n = rowi % N;
+    const long long li = n * T + t;
+    float lp = -INFINITY, ls = -INFINITY;
+    if (live) {
+        lp = prefix_lse[li];
+        ls = suffix_lse[li];
+    }
+    const float M = fmaxf(lp, ls);
+    float wp = 0.f, ws = 0.f, total = -INFINITY;
+    if (live && M != -INFINITY) {
+        wp = __builtin_amdgcn_exp2f((lp - M) * kLog2e);
+        ws = __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+        total = M + __builtin_amdgcn_logf(wp + ws) * kLn2;
+        const float inv = 1.0f / (wp + ws);
+        wp *= inv;
+        ws *= inv;
+    }
+    if (live) {
+        bf16x8 r = bf16x8{};
+        if (M != -INFINITY) {
+            const bf16x8 p = *(const bf16x8 *)(prefix_out + rowi * D + 8 * c);
+            const bf16x8 q = *(const bf16x8 *)(suffix_out + rowi * D + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 v = to_bf16x2(wp * (float)p[e] + ws * (float)q[e],
+                                           wp * (float)p[e + 1] + ws * (float)q[e + 1]);
+                r[e] = v[0];
+                r[e + 1] = v[1];
+            }
+        }
+        *(bf16x8 *)(out + rowi * D + 8 * c) = r;
+    }
+    __syncthreads();
+    if (live && c == 0 && out_lse)
+        out_lse[li] = total;
+}
+
+// ===========================================================================
 // host side
 // ===========================================================================
 bool valid_shape(const mla_decode_shape_t *s, mla_status_t *err)
@@ -1880,6 +2003,60 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *
     if (rows > 0 && (!part_out || !part_lse || !out))
         return MLA_ERR_NULL_POINTER;
     return launch_merge(rows, S, part_out, part_lse, out, lse, stream);
+}
+
+mla_status_t mla_gather_cache(int32_t num_tokens, const void *latent_cache, int32_t num_blocks,
+                              int32_t page_size, mla_cache_dtype_t cache_dtype,
+                              const float *cache_scale, const int32_t *block_table, int32_t batch,
+                              int32_t max_blocks_per_seq, const int32_t *cu_seq_lens,
+                              const int32_t *token_to_seq, const int32_t *seq_starts, void *dst,
+                              hipStream_t stream)
+{
+    if (num_tokens < 0 || num_blocks < 0 || page_size < 1 || batch < 0 ||
+        max_blocks_per_seq < 0)
+        return MLA_ERR_BAD_SHAPE;
+    if (cache_dtype != MLA_CACHE_BF16 && cache_dtype != MLA_CACHE_FP8_E4M3FN)
+        return MLA_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == MLA_CACHE_FP8_E4M3FN;
+    if (num_tokens == 0)
+        return MLA_OK;
+    if (batch < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return MLA_ERR_BAD_SHAPE;
+    if (!latent_cache || !block_table || !cu_seq_lens || !token_to_seq || !dst ||
+        (fp8 && !cache_scale))
+        return MLA_ERR_NULL_POINTER;
+    const long long n = (long long)num_tokens * 18;
+    const long long blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(mla_gather, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint8_t *)latent_cache, fp8 ? 1 : 0, cache_scale, block_table, batch,
+                       max_blocks_per_seq, num_blocks, page_size, cu_seq_lens, token_to_seq,
+                       seq_starts, (__bf16 *)dst, n);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_merge_attn_states(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                   const void *prefix_out, const float *prefix_lse,
+                                   const void *suffix_out, const float *suffix_lse, void *out,
+                                   float *out_lse, hipStream_t stream)
+{
+    if (num_tokens < 0 || num_heads < 0 || head_dim < 0)
+        return MLA_ERR_BAD_SHAPE;
+    if (head_dim < 8 || head_dim > 2048 || (head_dim & (head_dim - 1)) != 0)
+        return MLA_ERR_UNSUPPORTED;
+    if (num_tokens == 0 || num_heads == 0)
+        return MLA_OK;
+    if (!prefix_out || !prefix_lse || !suffix_out || !suffix_lse || !out)
+        return MLA_ERR_NULL_POINTER;
+    const long long n = (long long)num_tokens * num_heads * (head_dim / 8);
+    const long long blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(mla_merge_two, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const __bf16 *)prefix_out, prefix_lse, (const __bf16 *)suffix_out,
+                       suffix_lse, (__bf16 *)out, out_lse, num_tokens, num_heads, head_dim, n);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status_t mla_concat_q_insert_cache(int32_t num_tokens, int32_t num_heads,

@@ -31,7 +31,8 @@ HEAD_SIZE = KV_LORA_RANK + QK_ROPE_HEAD_DIM
 MAX_KV_SPLITS = 256
 
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
-            "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache")
+            "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache",
+            "mla_gather_cache", "mla_merge_attn_states")
 
 
 class MLAError(RuntimeError):
@@ -74,6 +75,10 @@ def load(path: Path | str | None = None):
                                         ctypes.c_float, i32, vp, sz, vp]
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_gather_cache.restype = ctypes.c_int
+    lib.mla_gather_cache.argtypes = [i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_merge_attn_states.restype = ctypes.c_int
+    lib.mla_merge_attn_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.mla_concat_q_insert_cache.restype = ctypes.c_int
     lib.mla_concat_q_insert_cache.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp,
                                               vp, vp, vp]
@@ -255,3 +260,54 @@ def concat_q_insert_cache(ql_nope, q_pe, kv_c, k_pe, latent_cache, slot_mapping,
         _ptr(q_out), _stream(ql_nope.device))
     _check(st, "mla_concat_q_insert_cache")
     return q_out
+
+
+def gather_cache(latent_cache, block_table, cu_seq_lens, token_to_seq, *, seq_starts=None,
+                 cache_scale=None, cache_dtype=None, dst=None):
+    """Chunked-context gather (mla_gather_cache): returns bf16 [num_tokens, 576]."""
+    n = int(token_to_seq.shape[0])
+    for name, t in (("block_table", block_table), ("cu_seq_lens", cu_seq_lens),
+                    ("token_to_seq", token_to_seq)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if seq_starts is not None and (seq_starts.dtype != torch.int32 or
+                                   not seq_starts.is_contiguous()):
+        raise ValueError("seq_starts must be a contiguous int32 tensor")
+    B, MB = int(block_table.shape[0]), int(block_table.shape[1])
+    if tuple(cu_seq_lens.shape) != (B + 1,):
+        raise ValueError("cu_seq_lens must be [batch + 1]")
+    dt = _cache_dtype(latent_cache, cache_dtype)
+    if dt == MLA_CACHE_FP8_E4M3FN and cache_scale is None:
+        raise ValueError("an fp8 cache needs cache_scale")
+    if dst is None:
+        dst = torch.empty((n, HEAD_SIZE), dtype=torch.bfloat16, device=latent_cache.device)
+    st = load().mla_gather_cache(n, _ptr(latent_cache), int(latent_cache.shape[0]),
+                                 int(latent_cache.shape[1]), dt,
+                                 _ptr(cache_scale) if dt == MLA_CACHE_FP8_E4M3FN else None,
+                                 _ptr(block_table), B, MB, _ptr(cu_seq_lens), _ptr(token_to_seq),
+                                 _ptr(seq_starts), _ptr(dst), _stream(latent_cache.device))
+    _check(st, "mla_gather_cache")
+    return dst
+
+
+def merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse, *, out=None, out_lse=None,
+                      return_lse=True):
+    """Two-state merge (mla_merge_attn_states): outputs bf16 [T, N, D], lse f32 [N, T].
+    out / out_lse may be the prefix (or suffix) tensors themselves."""
+    T, N, D = (int(x) for x in prefix_out.shape)
+    for name, t, dt, shape in (("prefix_out", prefix_out, torch.bfloat16, (T, N, D)),
+                               ("suffix_out", suffix_out, torch.bfloat16, (T, N, D)),
+                               ("prefix_lse", prefix_lse, torch.float32, (N, T)),
+                               ("suffix_lse", suffix_lse, torch.float32, (N, T))):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
+    if out is None:
+        out = torch.empty_like(prefix_out)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty_like(prefix_lse)
+    st = load().mla_merge_attn_states(T, N, D, _ptr(prefix_out), _ptr(prefix_lse),
+                                      _ptr(suffix_out), _ptr(suffix_lse), _ptr(out),
+                                      _ptr(out_lse if return_lse else None),
+                                      _stream(prefix_out.device))
+    _check(st, "mla_merge_attn_states")
+    return out, (out_lse if return_lse else None)

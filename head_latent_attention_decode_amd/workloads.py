@@ -287,3 +287,62 @@ def make_insert_inputs(T, N, num_blocks, page_size, *, seed, cache_dtype="bf16",
     return InsertInputs(ql_nope=ql_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe,
                         slot_mapping=torch.from_numpy(slots), cache=cache,
                         cache_scale_inv=inv, cache_dtype=cache_dtype)
+
+
+@dataclass
+class GatherInputs:
+    """A chunk of the requests' cached context, as a chunked prefill gathers it."""
+    block_table: torch.Tensor   # int32 [B, max_blocks]
+    cu_seq_lens: torch.Tensor   # int32 [B + 1]: request b's rows start at cu_seq_lens[b]
+    token_to_seq: torch.Tensor  # int32 [num_tokens]
+    seq_starts: torch.Tensor    # int32 [B]: first context token of the chunk, per request
+
+
+def make_gather_inputs(wl: Workload, *, seed, chunk_tokens, align=True) -> GatherInputs:
+    """One chunk over the workload's requests: request b contributes
+    min(chunk_tokens, L_b - start_b) rows from a random start_b inside its
+    context (a multiple of the page size when align is set, as the pages'
+    gather requires; any token otherwise)."""
+    rng = np.random.default_rng(seed)
+    lens = wl.seq_lens.numpy().astype(np.int64)
+    starts = np.zeros(wl.B, dtype=np.int64)
+    counts = np.zeros(wl.B, dtype=np.int64)
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        s = int(rng.integers(0, L))
+        if align:
+            s -= s % wl.page_size
+        starts[b] = s
+        counts[b] = min(int(chunk_tokens), int(L) - s)
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tts = np.repeat(np.arange(wl.B, dtype=np.int32), counts)
+    return GatherInputs(block_table=wl.block_table, cu_seq_lens=torch.from_numpy(cu),
+                        token_to_seq=torch.from_numpy(tts),
+                        seq_starts=torch.from_numpy(starts.astype(np.int32)))
+
+
+@dataclass
+class MergeInputs:
+    """Two partial attention states per (token, head), prefill layout."""
+    prefix_out: torch.Tensor    # bfloat16 [T, N, D]
+    prefix_lse: torch.Tensor    # float32 [N, T]
+    suffix_out: torch.Tensor    # bfloat16 [T, N, D]
+    suffix_lse: torch.Tensor    # float32 [N, T]
+
+
+def make_merge_inputs(T, N, D, *, seed, empty_frac=0.1) -> MergeInputs:
+    """Outputs N(0, 1) rounded to bf16; lse N(0, 3^2) in float32; a fraction
+    empty_frac of the states of each side have lse = -inf (no weight), and
+    the first token has both sides empty."""
+    g = torch.Generator().manual_seed(seed)
+    po = torch.randn(T, N, D, generator=g).to(torch.bfloat16)
+    so = torch.randn(T, N, D, generator=g).to(torch.bfloat16)
+    pl = torch.randn(N, T, generator=g) * 3
+    sl = torch.randn(N, T, generator=g) * 3
+    pl[torch.rand(N, T, generator=g) < empty_frac] = -float("inf")
+    sl[torch.rand(N, T, generator=g) < empty_frac] = -float("inf")
+    if T:
+        pl[:, 0] = -float("inf")
+        sl[:, 0] = -float("inf")
+    return MergeInputs(prefix_out=po, prefix_lse=pl, suffix_out=so, suffix_lse=sl)

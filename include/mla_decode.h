@@ -189,6 +189,64 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
                               void *out, float *lse, hipStream_t stream);
 
 /*
+ * Chunked-context gather (vLLM API docs, mla_attention, _compute_prefill_context,
+ * section "Chunked Prefill" of the module docstring): copies a chunk of the
+ * requests' cached context rows out of the paged cache into a contiguous
+ * workspace, dequantizing an fp8 cache on the way (the gather_and_maybe_
+ * dequant_cache step).  Workspace row i belongs to request b = token_to_seq[i]
+ * and holds that request's token
+ *     seq_starts[b] + (i - cu_seq_lens[b])          (seq_starts NULL: 0)
+ * found through block_table like the decode path.  A bf16 cache is copied
+ * bit for bit; an fp8 element becomes bf16(code_value * cache_scale), the
+ * product in fp32, rounded to nearest even.  The pages' gather needs chunk
+ * starts aligned to page_size; this one takes any start.
+ *
+ *   num_tokens        rows to write (>= 0).
+ *   latent_cache      device, [num_blocks, page_size, 576] bf16 or E4M3FN.
+ *   cache_scale       device, one float (fp8 only).
+ *   block_table       device, int32 [batch, max_blocks_per_seq].
+ *   cu_seq_lens       device, int32 [batch + 1]: request b's rows start at
+ *                     cu_seq_lens[b].
+ *   token_to_seq      device, int32 [num_tokens].
+ *   seq_starts        device, int32 [batch], or NULL.
+ *   dst               device, bf16 [num_tokens, 576].
+ * Device-data preconditions (not checked): the indices are consistent and
+ * name valid pages; out-of-range values are clamped so that every read stays
+ * in bounds, and the row is then unspecified.  Errors as for the other entry
+ * points; nothing is launched on an error.
+ */
+mla_status_t mla_gather_cache(int32_t num_tokens, const void *latent_cache, int32_t num_blocks,
+                              int32_t page_size, mla_cache_dtype_t cache_dtype,
+                              const float *cache_scale, const int32_t *block_table,
+                              int32_t batch, int32_t max_blocks_per_seq,
+                              const int32_t *cu_seq_lens, const int32_t *token_to_seq,
+                              const int32_t *seq_starts, void *dst, hipStream_t stream);
+
+/*
+ * Two-state LSE merge with the prefill layout (vLLM API docs, merge_attn_states
+ * as called by accumulate_mla_context_chunk, and the chunked-prefill listing
+ * of the mla_attention module docstring): for every token t and head n
+ *     M   = max(prefix_lse[n, t], suffix_lse[n, t])
+ *     wp  = exp(prefix_lse - M),  ws = exp(suffix_lse - M)
+ *     out = (wp * prefix_out[t, n, :] + ws * suffix_out[t, n, :]) / (wp + ws)
+ *     out_lse[n, t] = M + ln(wp + ws)
+ * A state with lse = -inf carries no weight and its output is not read; two
+ * such states give out = 0, lse = -inf.
+ *
+ *   prefix_out, suffix_out, out   device, bf16 [T, N, head_dim]; out may be
+ *                                 the same buffer as either input.
+ *   prefix_lse, suffix_lse        device, float [N, T] (natural log).
+ *   out_lse                       device, float [N, T], or NULL; may be the
+ *                                 same buffer as either input lse.
+ *   head_dim                      a power of two in [8, 2048], else
+ *                                 MLA_ERR_UNSUPPORTED.
+ */
+mla_status_t mla_merge_attn_states(int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                                   const void *prefix_out, const float *prefix_lse,
+                                   const void *suffix_out, const float *suffix_lse,
+                                   void *out, float *out_lse, hipStream_t stream);
+
+/*
  * The step before the attention of a decode step: form the absorbed query and
  * insert the step's new latent row into the paged cache, in one launch
  * (raon-1-mini mla_attention.py, the model-layer page, decode path of forward

@@ -76,6 +76,11 @@ def _declare(lib):
     lib.oracle_merge_states.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_e4m3fn_from_float.restype = ctypes.c_uint8
     lib.oracle_e4m3fn_from_float.argtypes = [ctypes.c_float]
+    lib.oracle_gather.restype = None
+    lib.oracle_gather.argtypes = [i32, i32, P, i32, i32, i32, ctypes.c_float, P, i32, i32, P, P,
+                                  P, P]
+    lib.oracle_merge_two.restype = None
+    lib.oracle_merge_two.argtypes = [i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_concat_insert.restype = None
     lib.oracle_concat_insert.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32, i32, i32,
                                          ctypes.c_float, P, P]
@@ -224,3 +229,36 @@ def concat_insert(ql_nope, q_pe, kv_c, k_pe, slot_mapping, cache, scale_inv=1.0,
         1 if cache.dtype == np.uint8 else 0, float(np.float32(scale_inv)), _ptr(cache),
         _ptr(q_out))
     return q_out
+
+
+def gather(cache, block_table, cu_seq_lens, token_to_seq, seq_starts=None, scale=1.0, lib=None):
+    """Chunked-context gather (see mla_oracle.c): returns uint16 bf16 bits
+    [num_tokens, D].  cache: uint16 (bf16 bits) or uint8 (E4M3FN codes)
+    [num_blocks, page_size, D]."""
+    cache = np.ascontiguousarray(cache)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seq_lens, dtype=np.int32)
+    tts = np.ascontiguousarray(token_to_seq, dtype=np.int32)
+    st = None if seq_starts is None else np.ascontiguousarray(seq_starts, dtype=np.int32)
+    nb, P, D = cache.shape
+    n = tts.shape[0]
+    dst = np.zeros((n, D), dtype=np.uint16)
+    (lib or load()).oracle_gather(n, D, _ptr(cache), nb, P, 1 if cache.dtype == np.uint8 else 0,
+                                  float(np.float32(scale)), _ptr(bt), bt.shape[0], bt.shape[1],
+                                  _ptr(cu), _ptr(tts), None if st is None else _ptr(st),
+                                  _ptr(dst))
+    return dst
+
+
+def merge_two(prefix_out, prefix_lse, suffix_out, suffix_lse, lib=None):
+    """Two-state merge: outputs [T, N, D], lse [N, T]; returns (out, lse) in fp64."""
+    po = np.ascontiguousarray(prefix_out, dtype=np.float64)
+    so = np.ascontiguousarray(suffix_out, dtype=np.float64)
+    pl = np.ascontiguousarray(prefix_lse, dtype=np.float64)
+    sl = np.ascontiguousarray(suffix_lse, dtype=np.float64)
+    T, N, D = po.shape
+    out = np.zeros((T, N, D))
+    lse = np.zeros((N, T))
+    (lib or load()).oracle_merge_two(T, N, D, _ptr(po), _ptr(pl), _ptr(so), _ptr(sl), _ptr(out),
+                                     _ptr(lse))
+    return out, lse

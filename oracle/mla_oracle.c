@@ -441,3 +441,91 @@ void oracle_concat_insert(int T, int N, int Dn, int Dr, const uint16_t *ql_nope,
         }
     }
 }
+
+/* ---- chunked-context gather and the two-state merge ----------------------
+ *
+ * vLLM API docs, mla_attention, _compute_prefill_context ("Chunked Prefill"):
+ * the context of the requests being prefilled is processed in chunks; each
+ * chunk's rows are first copied out of the paged cache into a contiguous
+ * workspace (gather_and_maybe_dequant_cache, with the chunk's per-request
+ * start seq_starts, the workspace offsets cu_seq_lens and the owner of each
+ * workspace row token_to_seq; an fp8 cache is dequantized on the way with
+ * its scale), then attended, and the chunk's partial (output, lse) is folded
+ * into the running one with merge_attn_states (accumulate_mla_context_chunk),
+ * whose LSE layout is [heads, tokens].  The module docstring's chunked
+ * prefill listing merges the same way: the state with the larger lse
+ * dominates, and the merged lse is the log of the summed exponentials.
+ *
+ * Readings:
+ *   - workspace row i belongs to request b = token_to_seq[i] and holds token
+ *     seq_starts[b] + (i - cu_seq_lens[b]) of that request, found through the
+ *     page table; a page-table entry outside [0, num_blocks) is clamped (the
+ *     GPU side reads in bounds whatever the table holds);
+ *   - an fp8 element is dequantized as the fp32 product code_value * scale,
+ *     rounded to bf16 (nearest even): where a float decides the stored bits
+ *     both sides decide in fp32;
+ *   - the merge of two states of weight zero (both lse = -inf) is out = 0,
+ *     lse = -inf, as for the S-way merge.
+ */
+
+/* bf16 bits of a float, round to nearest even (finite inputs and NaN). */
+static uint16_t bf16_from_float(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu))
+        return (uint16_t)((u >> 16) | 0x40);
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* dst [num_tokens, D] bf16 bits; cache [num_blocks, page_size, D] bf16 bits
+ * or E4M3FN codes; block_table [B, max_blocks]. */
+void oracle_gather(int num_tokens, int D, const void *cache, int num_blocks, int page_size,
+                   int fp8, float scale, const int32_t *block_table, int B, int max_blocks,
+                   const int32_t *cu_seq_lens, const int32_t *token_to_seq,
+                   const int32_t *seq_starts, uint16_t *dst)
+{
+    for (int i = 0; i < num_tokens; ++i) {
+        const int b = token_to_seq[i];
+        const int64_t pos = (int64_t)(seq_starts ? seq_starts[b] : 0) + (i - cu_seq_lens[b]);
+        int64_t pg = pos / page_size;
+        pg = pg < 0 ? 0 : (pg >= max_blocks ? max_blocks - 1 : pg);
+        int blk = block_table[(int64_t)b * max_blocks + pg];
+        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
+        const int64_t row = (int64_t)blk * page_size + pos % page_size;
+        for (int d = 0; d < D; ++d) {
+            if (!fp8) {
+                dst[(int64_t)i * D + d] = ((const uint16_t *)cache)[row * D + d];
+            } else {
+                const float v = (float)oracle_e4m3fn_to_double(((const uint8_t *)cache)[row * D + d]);
+                dst[(int64_t)i * D + d] = bf16_from_float(v * scale);
+            }
+        }
+    }
+}
+
+/* Two states per (token, head): outputs [T, N, D] as doubles, lse [N, T]. */
+void oracle_merge_two(int T, int N, int D, const double *prefix_out, const double *prefix_lse,
+                      const double *suffix_out, const double *suffix_lse, double *out,
+                      double *out_lse)
+{
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < N; ++n) {
+            const double lp = prefix_lse[(int64_t)n * T + t], ls = suffix_lse[(int64_t)n * T + t];
+            const double m = lp > ls ? lp : ls;
+            double *o = out + ((int64_t)t * N + n) * D;
+            const double *po = prefix_out + ((int64_t)t * N + n) * D;
+            const double *so = suffix_out + ((int64_t)t * N + n) * D;
+            if (m == -INFINITY) {
+                for (int d = 0; d < D; ++d)
+                    o[d] = 0.0;
+                out_lse[(int64_t)n * T + t] = -INFINITY;
+                continue;
+            }
+            const double wp = exp(lp - m), ws = exp(ls - m);
+            for (int d = 0; d < D; ++d)
+                o[d] = (wp * po[d] + ws * so[d]) / (wp + ws);
+            out_lse[(int64_t)n * T + t] = m + log(wp + ws);
+        }
+}

@@ -1,0 +1,78 @@
+"""Pins of the oracle's chunked-context gather and two-state merge.
+
+The gather is checked against a second formulation (a request's context laid
+out by concatenating its pages in table order, then sliced) and, for fp8,
+against torch's E4M3FN -> float -> bf16 conversion as a library reference.
+The two-state merge is checked against the S-way merge (itself pinned by
+split invariance), the neutral state, symmetry and the empty case.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_latent_attention_decode_amd import workloads as W
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _cache_np(wl):
+    return _bits(wl.cache) if wl.cache_dtype == "bf16" else wl.cache.numpy()
+
+
+@pytest.mark.parametrize("cache_dtype,align", [("bf16", True), ("bf16", False),
+                                               ("fp8_e4m3fn", True)])
+def test_gather_rows_are_the_requests_tokens(cache_dtype, align):
+    wl = W.make_workload(3, 16, 16, [70, 33, 140], seed=21, cache_dtype=cache_dtype)
+    g = W.make_gather_inputs(wl, seed=5, chunk_tokens=40, align=align)
+    got = oracle.gather(_cache_np(wl), g.block_table.numpy(), g.cu_seq_lens.numpy(),
+                        g.token_to_seq.numpy(), g.seq_starts.numpy(), scale=wl.cache_scale)
+    cache = wl.cache
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        npg = -(-L // wl.page_size)
+        seq = torch.cat([cache[int(p)] for p in wl.block_table[b, :npg]])[:L]   # [L, 576]
+        lo, hi = int(g.cu_seq_lens[b]), int(g.cu_seq_lens[b + 1])
+        s = int(g.seq_starts[b])
+        rows = seq[s: s + (hi - lo)]
+        if cache_dtype == "bf16":
+            want = _bits(rows)
+        else:
+            vals = rows.view(torch.float8_e4m3fn).float() * torch.tensor(wl.cache_scale)
+            want = _bits(vals.to(torch.bfloat16))
+        assert (got[lo:hi] == want).all(), b
+
+
+def test_merge_two_equals_s_way_merge():
+    m = W.make_merge_inputs(7, 3, 16, seed=4)
+    po = m.prefix_out.double().numpy()
+    so = m.suffix_out.double().numpy()
+    pl, sl = m.prefix_lse.double().numpy(), m.suffix_lse.double().numpy()
+    out, lse = oracle.merge_two(po, pl, so, sl)
+    T, N, D = po.shape
+    part_out = np.stack([po, so], axis=2).reshape(T * N, 2, D)
+    part_lse = np.stack([pl.T, sl.T], axis=2).reshape(T * N, 2)
+    ref_o, ref_l = oracle.merge_states(part_out, part_lse)
+    assert np.allclose(out.reshape(T * N, D), ref_o, rtol=1e-13, atol=1e-13)
+    live = np.isfinite(ref_l)
+    assert np.allclose(lse.T.reshape(-1)[live], ref_l[live], rtol=0, atol=1e-13)
+    assert (np.isneginf(lse.T.reshape(-1)) == ~live).all()
+
+
+def test_merge_two_neutral_symmetric_and_empty():
+    m = W.make_merge_inputs(5, 2, 8, seed=8, empty_frac=0.0)
+    po, so = m.prefix_out.double().numpy(), m.suffix_out.double().numpy()
+    pl, sl = m.prefix_lse.double().numpy(), m.suffix_lse.double().numpy()
+    ninf = np.full_like(pl, -np.inf)
+    o, l = oracle.merge_two(po, pl, np.full_like(so, 7.0), ninf)
+    assert (o[1:] == po[1:]).all() and (l[:, 1:] == pl[:, 1:]).all()   # (x, -inf) is neutral
+    a, la = oracle.merge_two(po, pl, so, sl)
+    b, lb = oracle.merge_two(so, sl, po, pl)
+    assert np.allclose(a[1:], b[1:], rtol=1e-14, atol=1e-14) and np.allclose(la[:, 1:], lb[:, 1:])
+    assert (a[0] == 0).all() and np.isneginf(la[:, 0]).all()          # both empty
+    # equal lse: the plain average, lse + ln 2
+    e, le = oracle.merge_two(po, pl, so, pl)
+    assert np.allclose(e[1:], (po[1:] + so[1:]) / 2, rtol=1e-14, atol=1e-14)
+    assert np.allclose(le[:, 1:], pl[:, 1:] + np.log(2.0), rtol=0, atol=1e-14)
