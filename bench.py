@@ -168,11 +168,14 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--cpu-requests", type=int, default=8,
                     help="requests in the CPU-oracle sample (0 disables it)")
-    ap.add_argument("--op", default="decode", choices=["decode", "insert", "gather", "merge2"],
+    ap.add_argument("--op", default="decode",
+                    choices=["decode", "insert", "gather", "merge2", "multi"],
                     help="decode: the attention step (default); insert: the decode step's "
                          "query concat and cache insert at the workload's B and N; gather: "
                          "the chunked-context gather of the workload's whole context; "
-                         "merge2: the two-state merge of prefill partials")
+                         "merge2: the two-state merge of prefill partials; multi: "
+                         "multi-token (speculative) decode with --qlen query rows per request")
+    ap.add_argument("--qlen", type=int, default=4, help="query rows per request for --op multi")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -202,6 +205,9 @@ def main():
         return
     if args.op == "merge2":
         run_merge2(args)
+        return
+    if args.op == "multi":
+        run_multi(args)
         return
 
     wl = W.config_workload(args.workload)
@@ -500,6 +506,60 @@ def run_merge2(args):
                     args.steps, args.warmup, "mla_merge_two",
                     f"merge2: T={T} tokens x N={N} heads x D={D}, bf16 states, [N, T] lse",
                     "bf16 states, fp32 lse", cpu)
+    print(json.dumps(line), flush=True)
+
+
+def run_multi(args):
+    """Multi-token (speculative) decode, causal, q_len query rows per request of
+    the workload.  Algorithmic bytes: every KV row once (the rows of a request
+    share it), the q_len * N queries and outputs, LSEs, page table, lengths;
+    flops: 2 * (576 + 512) per head per visible token of each query row."""
+    wl = W.config_workload(args.workload)
+    QL = args.qlen
+    S = args.splits or wl.num_kv_splits
+    dev = torch.device("cuda:0")
+    copies = []
+    for c in range(max(1, args.copies)):
+        g = torch.Generator().manual_seed(700 + c)
+        q = torch.randn(wl.B, QL, wl.N, W.HEAD_SIZE, generator=g).to(torch.bfloat16).to(dev)
+        d = dict(q=q, latent_cache=wl.cache.to(dev), block_table=wl.block_table.to(dev),
+                 seq_lens=wl.seq_lens.to(dev), softmax_scale=wl.softmax_scale,
+                 num_kv_splits=S, causal=True,
+                 cache_scale=(torch.tensor([wl.cache_scale], dtype=torch.float32, device=dev)
+                              if wl.cache_dtype == "fp8_e4m3fn" else None),
+                 cache_dtype=wl.cache_dtype)
+        d["out"] = torch.empty(wl.B, QL, wl.N, W.KV_LORA_RANK, dtype=torch.bfloat16, device=dev)
+        d["lse"] = torch.empty(wl.B, QL, wl.N, dtype=torch.float32, device=dev)
+        ws = mla.load().mla_decode_multi_workspace_size(
+            ctypes.byref(mla.make_shape(q.view(wl.B, QL * wl.N, -1), d["latent_cache"],
+                                        d["block_table"], wl.cache_dtype)), QL, S)
+        d["workspace"] = torch.empty(max(1, int(ws)), dtype=torch.uint8, device=dev)
+        copies.append(d)
+    calls = [(lambda d=d: mla.mla_decode_multi(**d)) for d in copies]
+    call_ms, wall = _time_calls(calls, args.warmup, args.steps)
+    lens = wl.seq_lens.to(torch.int64)
+    esz = 1 if wl.cache_dtype == "fp8_e4m3fn" else 2
+    pages = int(((lens + wl.page_size - 1) // wl.page_size).sum())
+    rows = wl.B * QL * wl.N
+    nbytes = int(lens.sum()) * W.HEAD_SIZE * esz + rows * (W.HEAD_SIZE * 2 + W.KV_LORA_RANK * 2
+                                                           + 4) + 4 * pages + 4 * wl.B
+    vis = sum(max(0, int(L) - (QL - 1 - j)) for L in lens.tolist() for j in range(QL))
+    flops = 2 * (W.HEAD_SIZE + W.KV_LORA_RANK) * wl.N * vis
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    line = _op_line("multi-token decode TFLOP/s (% of bf16 MFMA roofline)", nbytes, call_ms,
+                    wall, args.steps, args.warmup, "mla_decode_multi (split + merge)",
+                    f"multi: {wl.name}, B={wl.B} requests x q_len={QL} causal x N={wl.N} "
+                    f"heads, num_kv_splits={S}, {wl.cache_dtype} cache",
+                    "bf16", None, {"q_len": QL, "algorithmic_flops": flops})
+    line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
+                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "mla_decode_multi (split + merge)",
+                        "kernel_ms": round(call_ms, 5),
+                        "hbm_frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    line["metric"] = "multi-token decode TFLOP/s (% of bf16 MFMA roofline)"
+    line["value"] = round(flops / (wall / args.steps) / 1e12, 2)
+    line["unit"] = "TFLOP/s"
     print(json.dumps(line), flush=True)
 
 

@@ -93,6 +93,10 @@ struct Params {
     float *lse;                 // [B, N] or null   (direct mode)
     float scale_log2;           // softmax_scale * log2(e)
     int B, N, S, MB, num_blocks, page_shift, HG;
+    // Query rows per request (multi-token decode): query row bq belongs to
+    // request bq / QL and is its new token bq % QL; causal rows see the
+    // request's first L - (QL - 1 - bq % QL) tokens, others all L.
+    int QL, causal;
 };
 
 // XOR swizzle of the 16-byte chunks of LDS row r (rows are 1152 bytes):
@@ -121,14 +125,19 @@ __device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int
     b = bs / p.S;
 }
 
-// Token range [t0, t1) of split s of request b.  The chunk length is
+// Token range [t0, t1) of split s of query row bq (request bq / QL).  The
+// length L is the request's, less the later new tokens a causal row may not
+// see.  The chunk length is
 // ceil(L / S) rounded up to kSplitUnit and to at least kMinChunk, a function
 // of (L, S) only.
-__device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &t0, int &t1)
+__device__ __forceinline__ void chunk_range(const Params &p, int bq, int s, int &t0, int &t1)
 {
     const long long cap = (long long)p.MB << p.page_shift;
-    long long L = load_uniform(p.seq_lens, b);
+    long long L = load_uniform(p.seq_lens, bq / p.QL);
     L = L < 0 ? 0 : (L > cap ? cap : L);
+    if (p.causal)
+        L -= p.QL - 1 - bq % p.QL;
+    L = L < 0 ? 0 : L;
     const long long per = (L + p.S - 1) / p.S;
     long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
     C = C > kMinChunk ? C : kMinChunk;
@@ -515,10 +524,11 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
     using Cfg = WideCfg<NG, kFp8>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLds];
 
-    int b, s, hg;
-    decode_work(p, b, s, hg);
+    int bq, s, hg;
+    decode_work(p, bq, s, hg);
+    const int b = bq / p.QL;    // the request whose pages are read
     int t_begin, t_end;
-    chunk_range(p, b, s, t_begin, t_end);
+    chunk_range(p, bq, s, t_begin, t_end);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -530,7 +540,7 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
     ln.r32 = lane & 31;
     ln.g2 = lane >> 5;
     const int HB = 32 * NG;                                       // heads per workgroup
-    const long long head0 = (long long)b * p.N + hg * HB;        // row of head 0
+    const long long head0 = (long long)bq * p.N + hg * HB;       // row of head 0
     const long long qrow = head0 + 32 * g + 16 * ln.c + ln.r16;   // QK head
     const long long orow = head0 + 32 * g + ln.r32;               // PV head
 
@@ -919,14 +929,15 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsLds];
 
-    int b, s, hg;
-    decode_work(p, b, s, hg);
+    int bq, s, hg;
+    decode_work(p, bq, s, hg);
+    const int b = bq / p.QL;    // the request whose pages are read
     int t_begin, t_end;
-    chunk_range(p, b, s, t_begin, t_end);
+    chunk_range(p, bq, s, t_begin, t_end);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long head0 = (long long)b * p.N + hg * 64;
+    const long long head0 = (long long)bq * p.N + hg * 64;
 
     if (t_begin >= t_end) {
         // empty split: lse = -inf (its partial output is never read), or, when
@@ -1252,16 +1263,17 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveLds16];
 
-    int b, s, hg;
-    decode_work(p, b, s, hg);
+    int bq, s, hg;
+    decode_work(p, bq, s, hg);
+    const int b = bq / p.QL;    // the request whose pages are read
     int t_begin, t_end;
-    chunk_range(p, b, s, t_begin, t_end);
+    chunk_range(p, bq, s, t_begin, t_end);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
-    const long long row_b0 = (long long)b * p.N + hg * 16;   // first head's row
+    const long long row_b0 = (long long)bq * p.N + hg * 16;  // first head's row
 
     if (t_begin >= t_end) {
         // empty split: lse = -inf (its partial output is never read), or, when
@@ -1803,7 +1815,7 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
                           const float *cache_scale, const int32_t *block_table,
                           const int32_t *seq_lens, float softmax_scale, int S,
                           float *part_out, float *part_lse, void *out, float *lse,
-                          hipStream_t stream)
+                          hipStream_t stream, int q_len = 1, int causal = 1)
 {
     Params p;
     p.q = (const __bf16 *)q;
@@ -1822,6 +1834,8 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     p.MB = s->max_blocks_per_seq;
     p.num_blocks = s->num_blocks;
     p.page_shift = log2_int(s->page_size);
+    p.QL = q_len;
+    p.causal = causal;
     const bool direct = part_out == nullptr;
     const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
     // Kernel choice by head count and cache dtype:
@@ -1837,7 +1851,7 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     else if (fp8 && s->num_heads % 64 == 0)
         heads_per_wg = 64;
     p.HG = s->num_heads / heads_per_wg;
-    const long long grid = (long long)s->batch * S * p.HG;
+    const long long grid = (long long)s->batch * q_len * S * p.HG;
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
     const dim3 g((unsigned)grid);
@@ -1989,6 +2003,49 @@ mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
     float *part_lse = part_out + (size_t)shape->batch * shape->num_heads * num_kv_splits * kDV;
     return launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens, softmax_scale,
                         num_kv_splits, part_out, part_lse, nullptr, nullptr, stream);
+}
+
+size_t mla_decode_multi_workspace_size(const mla_decode_shape_t *shape, int32_t q_len,
+                                       int32_t num_kv_splits)
+{
+    if (!shape || q_len < 1 || q_len > MLA_MAX_QUERY_LEN)
+        return 0;
+    mla_decode_shape_t v = *shape;
+    v.batch = shape->batch * q_len;
+    return mla_decode_workspace_size(&v, num_kv_splits);
+}
+
+mla_status_t mla_decode_multi(const mla_decode_shape_t *shape, int32_t q_len, int32_t causal,
+                              const void *q, const void *latent_cache, const float *cache_scale,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              float softmax_scale, int32_t num_kv_splits, void *workspace,
+                              size_t workspace_bytes, void *out, float *lse, hipStream_t stream)
+{
+    if (q_len < 1 || q_len > MLA_MAX_QUERY_LEN)
+        return MLA_ERR_BAD_SHAPE;
+    mla_status_t err = check_common(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                                    num_kv_splits);
+    if (err != MLA_OK)
+        return err;
+    if (shape->batch > 0 && !out)
+        return MLA_ERR_NULL_POINTER;
+    const size_t need = mla_decode_multi_workspace_size(shape, q_len, num_kv_splits);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MLA_ERR_WORKSPACE;
+    if (shape->batch == 0)
+        return MLA_OK;
+    const int c = causal ? 1 : 0;
+    if (num_kv_splits == 1)
+        return launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                            softmax_scale, 1, nullptr, nullptr, out, lse, stream, q_len, c);
+    const size_t rows = (size_t)shape->batch * q_len * shape->num_heads;
+    float *part_out = (float *)workspace;
+    float *part_lse = part_out + rows * num_kv_splits * kDV;
+    err = launch_split(shape, q, latent_cache, cache_scale, block_table, seq_lens, softmax_scale,
+                       num_kv_splits, part_out, part_lse, nullptr, nullptr, stream, q_len, c);
+    if (err != MLA_OK)
+        return err;
+    return launch_merge((int)rows, num_kv_splits, part_out, part_lse, out, lse, stream);
 }
 
 mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *part_out,

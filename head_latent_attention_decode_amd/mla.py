@@ -32,7 +32,8 @@ MAX_KV_SPLITS = 256
 
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
             "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache",
-            "mla_gather_cache", "mla_merge_attn_states")
+            "mla_gather_cache", "mla_merge_attn_states", "mla_decode_multi_workspace_size",
+            "mla_decode_multi")
 
 
 class MLAError(RuntimeError):
@@ -75,6 +76,11 @@ def load(path: Path | str | None = None):
                                         ctypes.c_float, i32, vp, sz, vp]
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_decode_multi_workspace_size.restype = sz
+    lib.mla_decode_multi_workspace_size.argtypes = [ctypes.POINTER(DecodeShape), i32, i32]
+    lib.mla_decode_multi.restype = ctypes.c_int
+    lib.mla_decode_multi.argtypes = [ctypes.POINTER(DecodeShape), i32, i32, vp, vp, vp, vp, vp,
+                                     ctypes.c_float, i32, vp, sz, vp, vp, vp]
     lib.mla_gather_cache.restype = ctypes.c_int
     lib.mla_gather_cache.argtypes = [i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.mla_merge_attn_states.restype = ctypes.c_int
@@ -176,6 +182,37 @@ def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_spl
                            int(num_kv_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
                            _stream(dev))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_multi(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
+                     causal=True, cache_scale=None, cache_dtype=None, out=None, lse=None,
+                     return_lse=True, workspace=None):
+    """Multi-token decode: q bf16 [B, q_len, N, 576] -> (out bf16 [B, q_len, N, 512],
+    lse f32 [B, q_len, N] or None).  seq_lens count the q_len new tokens."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q_len, N, 576]")
+    B, QL, N, D = (int(x) for x in q.shape)
+    _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale)
+    shape = make_shape(q.view(B, QL * N, D), latent_cache, block_table, cache_dtype)
+    shape.num_heads = N
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, QL, N, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, QL, N), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    need = int(load().mla_decode_multi_workspace_size(ctypes.byref(shape), QL,
+                                                      int(num_kv_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().mla_decode_multi(ctypes.byref(shape), QL, 1 if causal else 0, _ptr(q),
+                                 _ptr(latent_cache), _ptr(cache_scale), _ptr(block_table),
+                                 _ptr(seq_lens), float(softmax_scale), int(num_kv_splits),
+                                 _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(dev))
+    _check(st, "mla_decode_multi")
     return out, lse
 
 

@@ -89,6 +89,7 @@ typedef enum {
 #define MLA_KV_LORA_RANK 512
 #define MLA_QK_ROPE_HEAD_DIM 64
 #define MLA_MAX_KV_SPLITS 256
+#define MLA_MAX_QUERY_LEN 16
 
 typedef struct {
     int32_t batch;              /* B >= 0 requests, one query token each */
@@ -186,6 +187,38 @@ mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
  */
 mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
                               const float *part_out, const float *part_lse,
+                              void *out, float *lse, hipStream_t stream);
+
+/*
+ * Multi-token decode (speculative decoding with a uniform query length; vLLM
+ * API docs, mla_attention, QueryLenSupport "UNIFORM": every request of the
+ * batch has the same q_len > 1 new tokens; the metadata builder's causal /
+ * non-causal multi-token decode).  Request b has seq_lens[b] = L tokens in
+ * the cache, its q_len new ones included (their rows are inserted before the
+ * attention).  Query row j (0 <= j < q_len) of request b is the absorbed query
+ * of its new token j and attends over
+ *     causal != 0:  tokens [0, L - q_len + 1 + j)   (itself and what precedes)
+ *     causal == 0:  tokens [0, L)
+ * with the same definition, splitting and merge as mla_decode.  A row whose
+ * range is empty gives out = 0, lse = -inf.
+ *
+ *   q_len        1 .. MLA_MAX_QUERY_LEN query rows per request.
+ *   q            device, bf16 [batch, q_len, num_heads, 576].
+ *   out          device, bf16 [batch, q_len, num_heads, 512].
+ *   lse          device, float [batch, q_len, num_heads], or NULL.
+ *   workspace    mla_decode_multi_workspace_size(shape, q_len, S) bytes
+ *                (0 when S == 1).
+ * Other arguments and errors as for mla_decode; q_len outside the range
+ * gives MLA_ERR_BAD_SHAPE.  Each query row reads its request's rows through
+ * the L2 of the XCD its workgroups share with the request's other rows.
+ */
+size_t mla_decode_multi_workspace_size(const mla_decode_shape_t *shape, int32_t q_len,
+                                       int32_t num_kv_splits);
+mla_status_t mla_decode_multi(const mla_decode_shape_t *shape, int32_t q_len, int32_t causal,
+                              const void *q, const void *latent_cache,
+                              const float *cache_scale, const int32_t *block_table,
+                              const int32_t *seq_lens, float softmax_scale,
+                              int32_t num_kv_splits, void *workspace, size_t workspace_bytes,
                               void *out, float *lse, hipStream_t stream);
 
 /*

@@ -262,3 +262,30 @@ def merge_two(prefix_out, prefix_lse, suffix_out, suffix_lse, lib=None):
     (lib or load()).oracle_merge_two(T, N, D, _ptr(po), _ptr(pl), _ptr(so), _ptr(sl), _ptr(out),
                                      _ptr(lse))
     return out, lse
+
+
+def mla_decode_multi(q, cache, block_table, seq_lens, softmax_scale, q_len, causal=True,
+                     cache_scale=1.0, nthreads=None, lib=None):
+    """Multi-token decode with a uniform query length (vLLM API docs,
+    QueryLenSupport "UNIFORM"; causal or not among the new tokens).
+
+    q float64 [B, q_len, N, Dqk]; seq_lens [B] count the q_len new tokens.
+    Query row j of request b is an ordinary single-token decode row over the
+    request's first L_b - (q_len - 1 - j) tokens when causal (its own token
+    and those before it), over all L_b otherwise; a length below 0 is 0.
+    Returns (out [B, q_len, N, Dv], lse [B, q_len, N]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, QL, N, D = q.shape
+    if QL != q_len:
+        raise ValueError("q's second axis must be q_len")
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    row_lens = np.repeat(lens, q_len)
+    if causal:
+        row_lens = row_lens - (q_len - 1 - np.tile(np.arange(q_len), B))
+    row_lens = np.maximum(row_lens, 0).astype(np.int32)
+    prob = Problem(q.reshape(B * q_len, N, D), cache, np.repeat(np.asarray(block_table), q_len,
+                                                                axis=0),
+                   row_lens, softmax_scale, cache_scale)
+    out, lse = mla_decode(prob, nthreads=nthreads, lib=lib)
+    return out.reshape(B, q_len, N, -1), lse.reshape(B, q_len, N)
