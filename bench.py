@@ -169,12 +169,14 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8,
                     help="requests in the CPU-oracle sample (0 disables it)")
     ap.add_argument("--op", default="decode",
-                    choices=["decode", "insert", "gather", "merge2", "multi"],
+                    choices=["decode", "insert", "gather", "merge2", "multi", "absorb", "upproj"],
                     help="decode: the attention step (default); insert: the decode step's "
                          "query concat and cache insert at the workload's B and N; gather: "
                          "the chunked-context gather of the workload's whole context; "
                          "merge2: the two-state merge of prefill partials; multi: "
-                         "multi-token (speculative) decode with --qlen query rows per request")
+                         "multi-token (speculative) decode with --qlen query rows per request; "
+                         "absorb / upproj: the per-head W_UK_T / W_UV matmuls at the "
+                         "workload's B and N")
     ap.add_argument("--qlen", type=int, default=4, help="query rows per request for --op multi")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
@@ -208,6 +210,9 @@ def main():
         return
     if args.op == "multi":
         run_multi(args)
+        return
+    if args.op in ("absorb", "upproj"):
+        run_projection(args)
         return
 
     wl = W.config_workload(args.workload)
@@ -560,6 +565,40 @@ def run_multi(args):
     line["metric"] = "multi-token decode TFLOP/s (% of bf16 MFMA roofline)"
     line["value"] = round(flops / (wall / args.steps) / 1e12, 2)
     line["unit"] = "TFLOP/s"
+    print(json.dumps(line), flush=True)
+
+
+def run_projection(args):
+    """The per-head matmul before (absorb: q_nope . W_UK_T, K = 128 -> 512) or
+    after (upproj: latent . W_UV, K = 512 -> 128) the attention, for the
+    workload's B tokens and N heads.  Algorithmic bytes: the weights once
+    (N * K * M * 2), the activations in and the results out; flops 2 * B * N * K * M."""
+    spec = W.CONFIGS[args.workload]
+    B, N = spec["B"], spec["N"]
+    dev = torch.device("cuda:0")
+    absorb = args.op == "absorb"
+    K, M = (128, W.KV_LORA_RANK) if absorb else (W.KV_LORA_RANK, 128)
+    copies = []
+    for c in range(max(1, args.copies)):
+        x = W.make_projection_inputs(B, N, seed=800 + c)
+        if absorb:
+            d = (x.q_nope.to(dev), x.W_UK.permute(1, 2, 0).contiguous().to(dev))
+        else:
+            d = (x.latent_out.to(dev), x.W_UV.transpose(0, 1).contiguous().to(dev))
+        out = torch.empty(B, N, M, dtype=torch.bfloat16, device=dev)
+        copies.append((d, out))
+    fn = mla.absorb_query if absorb else mla.up_project
+    calls = [(lambda d=d, o=o: fn(d[0], d[1], out=o)) for d, o in copies]
+    kernel_ms, wall = _time_calls(calls, args.warmup, args.steps)
+    nbytes = N * K * M * 2 + B * N * (K + M) * 2
+    flops = 2 * B * N * K * M
+    name = "absorb (q_nope . W_UK_T)" if absorb else "up-projection (latent . W_UV)"
+    line = _op_line(f"per-head {name} GB/s (% of HBM roofline)", nbytes, kernel_ms, wall,
+                    args.steps, args.warmup, "mla_head_mm",
+                    f"{args.op}: B={B} tokens x N={N} heads, K={K} -> M={M}, bf16, "
+                    f"{args.workload} shapes", "bf16", None,
+                    {"tokens": B, "num_heads": N, "algorithmic_flops": flops})
+    line["roofline"]["tflops"] = round(flops / (kernel_ms * 1e-3) / 1e12, 2)
     print(json.dumps(line), flush=True)
 
 

@@ -1777,6 +1777,86 @@ __global__ __launch_bounds__(256) void mla_merge_two(
 }
 
 // ===========================================================================
+// Per-head matmuls around the attention: out[b, n, c] = sum_k x[b, n, k] *
+// W[n, k, c], the query absorb (K = 128, M = 512, W = W_UK_T) and the output
+// up-projection (K = 512, M = 128, W = W_UV).  One single-wave workgroup per
+// (head, 32-column block), so that several overlap on a CU while each stages
+// its block of W (K rows x 32 columns, rows padded to 80 bytes) in LDS.  The
+// block is read transposed with ds_read_b64_tr_b16 as the A operand of
+// v_mfma_f32_32x32x16_bf16 computing out^T = W^T . x^T, so a lane's results
+// are 4 consecutive columns of one row; the batch is walked 32 rows at a
+// time, each block's x slice (16 bytes per lane and k step) loaded into
+// registers at once.
+// ===========================================================================
+template <int K>
+__global__ __launch_bounds__(64) void mla_head_mm(const __bf16 *__restrict__ x, long long xs_tok,
+                                                  long long xs_head, const __bf16 *__restrict__ w,
+                                                  __bf16 *__restrict__ out, int B, int N, int M)
+{
+    constexpr int kRow = 80;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[K * kRow];
+    LDS_AS uint8_t *lds = AS3(smem);
+    const int nblk = M / 32;
+    const int n = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * 32;
+    const int lane = threadIdx.x;
+    const __bf16 *wn = w + (long long)n * K * M + c0;
+    const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
+    // the x fragments of one 32-row block, all K / 16 of them in registers;
+    // the first block's loads are in flight while W is staged
+    constexpr int kSteps = K / 16;
+    bf16x8 xf[kSteps];
+    auto load_x = [&](int rb) {
+        const int row = rb + r32;
+        const bool live = row < B;
+        const __bf16 *xr = x + (long long)(live ? row : 0) * xs_tok + (long long)n * xs_head + 8 * g2;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks)
+            xf[ks] = live ? *(const bf16x8 *)(xr + 16 * ks) : bf16x8{};
+    };
+    load_x(0);
+    // 4 chunks of 16 bytes per row: lane l stages chunk l & 3 of rows l >> 2, +16, ...
+#pragma unroll 8
+    for (int r = lane >> 2; r < K; r += 16)
+        *(LDS_AS bf16x8 *)(lds + r * kRow + (lane & 3) * 16) =
+            *(const bf16x8 *)(wn + (long long)r * M + 8 * (lane & 3));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    // group G loads rows 8(G >> 1) + 4h + (j >> 2) (+16 ks), columns
+    // 16(G & 1) + 4(j & 3) .. +4; lane j then holds column j of the group's 16
+    // (W^T row r32) at 4 consecutive rows (k)
+    int toff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        toff[h] = (8 * (G >> 1) + 4 * h + (j >> 2)) * kRow + (16 * (G & 1) + 4 * (j & 3)) * 2;
+    for (int rb = 0; rb < B; rb += 32) {
+        const int row = rb + r32;
+        const bool live = row < B;
+        if (rb > 0)
+            load_x(rb);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4 *)(lds + toff[0] + ks * 16 * kRow));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4 *)(lds + toff[1] + ks * 16 * kRow));
+            const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[ks], acc, 0, 0, 0);
+        }
+        // lane (r32, g2): batch row r32, columns 8q + 4g2 .. +4 of the block
+        if (live) {
+            __bf16 *o = out + ((long long)row * N + n) * M + c0 + 4 * g2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x2 p01 = to_bf16x2(acc[4 * q], acc[4 * q + 1]);
+                const bf16x2 p23 = to_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
+                *(bf16x4 *)(o + 8 * q) = bf16x4{p01[0], p01[1], p23[0], p23[1]};
+            }
+        }
+    }
+}
+
+// ===========================================================================
 // host side
 // ===========================================================================
 bool valid_shape(const mla_decode_shape_t *s, mla_status_t *err)
@@ -2060,6 +2140,50 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *
     if (rows > 0 && (!part_out || !part_lse || !out))
         return MLA_ERR_NULL_POINTER;
     return launch_merge(rows, S, part_out, part_lse, out, lse, stream);
+}
+
+static mla_status_t launch_head_mm(int K, int M, int32_t batch, int32_t num_heads, const void *x,
+                                   int64_t x_token_stride, int64_t x_head_stride, const void *w,
+                                   void *out, hipStream_t stream)
+{
+    if (batch < 0 || num_heads < 0 || x_token_stride < 0 || x_head_stride < 0)
+        return MLA_ERR_BAD_SHAPE;
+    if (batch == 0 || num_heads == 0)
+        return MLA_OK;
+    if (!x || !w || !out)
+        return MLA_ERR_NULL_POINTER;
+    // 16-byte loads of x and of W rows
+    if ((x_token_stride | x_head_stride) & 7 || ((uintptr_t)x & 15) || ((uintptr_t)w & 15) ||
+        ((uintptr_t)out & 7))
+        return MLA_ERR_UNSUPPORTED;
+    const long long grid = (long long)num_heads * (M / 32);
+    if (grid > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    if (K == 128)
+        hipLaunchKernelGGL(mla_head_mm<128>, dim3((unsigned)grid), dim3(64), 0, stream,
+                           (const __bf16 *)x, (long long)x_token_stride, (long long)x_head_stride,
+                           (const __bf16 *)w, (__bf16 *)out, batch, num_heads, M);
+    else
+        hipLaunchKernelGGL(mla_head_mm<512>, dim3((unsigned)grid), dim3(64), 0, stream,
+                           (const __bf16 *)x, (long long)x_token_stride, (long long)x_head_stride,
+                           (const __bf16 *)w, (__bf16 *)out, batch, num_heads, M);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_absorb_query(int32_t batch, int32_t num_heads, const void *q_nope,
+                              int64_t q_token_stride, int64_t q_head_stride, const void *w_uk_t,
+                              void *ql_nope, hipStream_t stream)
+{
+    return launch_head_mm(128, kDV, batch, num_heads, q_nope, q_token_stride, q_head_stride,
+                          w_uk_t, ql_nope, stream);
+}
+
+mla_status_t mla_up_project(int32_t batch, int32_t num_heads, const void *latent_out,
+                            int64_t x_token_stride, int64_t x_head_stride, const void *w_uv,
+                            void *out, hipStream_t stream)
+{
+    return launch_head_mm(kDV, 128, batch, num_heads, latent_out, x_token_stride, x_head_stride,
+                          w_uv, out, stream);
 }
 
 mla_status_t mla_gather_cache(int32_t num_tokens, const void *latent_cache, int32_t num_blocks,

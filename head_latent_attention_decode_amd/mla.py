@@ -33,7 +33,7 @@ MAX_KV_SPLITS = 256
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
             "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache",
             "mla_gather_cache", "mla_merge_attn_states", "mla_decode_multi_workspace_size",
-            "mla_decode_multi")
+            "mla_decode_multi", "mla_absorb_query", "mla_up_project")
 
 
 class MLAError(RuntimeError):
@@ -81,6 +81,10 @@ def load(path: Path | str | None = None):
     lib.mla_decode_multi.restype = ctypes.c_int
     lib.mla_decode_multi.argtypes = [ctypes.POINTER(DecodeShape), i32, i32, vp, vp, vp, vp, vp,
                                      ctypes.c_float, i32, vp, sz, vp, vp, vp]
+    for name in ("mla_absorb_query", "mla_up_project"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [i32, i32, vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
     lib.mla_gather_cache.restype = ctypes.c_int
     lib.mla_gather_cache.argtypes = [i32, vp, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.mla_merge_attn_states.restype = ctypes.c_int
@@ -348,3 +352,27 @@ def merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse, *, out=Non
                                       _stream(prefix_out.device))
     _check(st, "mla_merge_attn_states")
     return out, (out_lse if return_lse else None)
+
+
+def _head_mm(name, x, w, K, M, out):
+    if x.dim() != 3 or x.shape[2] != K or x.dtype != torch.bfloat16 or x.stride(2) != 1:
+        raise ValueError(f"x must be bf16 [B, N, {K}] with unit stride on the last axis")
+    B, N = int(x.shape[0]), int(x.shape[1])
+    if tuple(w.shape) != (N, K, M) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+        raise ValueError(f"weight must be a contiguous bf16 [N, {K}, {M}] tensor")
+    if out is None:
+        out = torch.empty((B, N, M), dtype=torch.bfloat16, device=x.device)
+    st = getattr(load(), name)(B, N, _ptr(x), int(x.stride(0)), int(x.stride(1)), _ptr(w),
+                               _ptr(out), _stream(x.device))
+    _check(st, name)
+    return out
+
+
+def absorb_query(q_nope, w_uk_t, out=None):
+    """ql_nope [B, N, 512] = per head q_nope [B, N, 128] . w_uk_t [N, 128, 512]."""
+    return _head_mm("mla_absorb_query", q_nope, w_uk_t, 128, KV_LORA_RANK, out)
+
+
+def up_project(latent_out, w_uv, out=None):
+    """out [B, N, 128] = per head latent_out [B, N, 512] . w_uv [N, 512, 128]."""
+    return _head_mm("mla_up_project", latent_out, w_uv, KV_LORA_RANK, 128, out)

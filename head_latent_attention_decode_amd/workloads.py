@@ -346,3 +346,24 @@ def make_merge_inputs(T, N, D, *, seed, empty_frac=0.1) -> MergeInputs:
         pl[:, 0] = -float("inf")
         sl[:, 0] = -float("inf")
     return MergeInputs(prefix_out=po, prefix_lse=pl, suffix_out=so, suffix_lse=sl)
+
+
+@dataclass
+class ProjectionInputs:
+    """Inputs of the per-head matmuls around the attention, in the pages' layouts."""
+    q_nope: torch.Tensor        # bfloat16 [B, N, 128]
+    latent_out: torch.Tensor    # bfloat16 [B, N, 512]
+    W_UK: torch.Tensor          # bfloat16 [512, N, 128]  (Lkv, N, P)
+    W_UV: torch.Tensor          # bfloat16 [512, N, 128]  (Lkv, N, V)
+
+
+def make_projection_inputs(B, N, *, seed, P=128, V=128) -> ProjectionInputs:
+    """Activations N(0, 1) and weights N(0, 1/Lkv) (so that products stay of
+    order one), all rounded to bf16."""
+    g = torch.Generator().manual_seed(seed)
+    q_nope = torch.randn(B, N, P, generator=g).to(torch.bfloat16)
+    latent = torch.randn(B, N, KV_LORA_RANK, generator=g).to(torch.bfloat16)
+    s = 1.0 / math.sqrt(KV_LORA_RANK)
+    W_UK = (torch.randn(KV_LORA_RANK, N, P, generator=g) * s).to(torch.bfloat16)
+    W_UV = (torch.randn(KV_LORA_RANK, N, V, generator=g) * s).to(torch.bfloat16)
+    return ProjectionInputs(q_nope=q_nope, latent_out=latent, W_UK=W_UK, W_UV=W_UV)

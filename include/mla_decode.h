@@ -190,6 +190,38 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
                               void *out, float *lse, hipStream_t stream);
 
 /*
+ * The per-head matmuls on either side of the attention (vLLM API docs,
+ * mla_attention, "Data-Movement Friendly Approach (i.e. forward_mqa)":
+ * ql_nope = q_nope . W_UK contracting P, then the latent output times W_UV;
+ * the decode path runs them as batched matmuls over the heads with the
+ * weights prepared once as W_UK_T = W_UK permuted to [N, P, Lkv] and W_UV
+ * transposed to [N, Lkv, V], as the MLA common page's weight processing
+ * does).  fp32 accumulation, bf16 results rounded to nearest even.
+ *
+ * mla_absorb_query:  ql_nope[b, n, l] = sum_p q_nope[b, n, p] * w_uk_t[n, p, l]
+ *   q_nope   device, bf16, element (b, n, p) at b * q_token_stride +
+ *            n * q_head_stride + p (P = 128; a slice of a wider query row is
+ *            fine: contiguous is q_token_stride = N * 128, q_head_stride = 128).
+ *   w_uk_t   device, bf16 [N, 128, 512], contiguous.
+ *   ql_nope  device, bf16 [batch, N, 512], contiguous.
+ * mla_up_project:    out[b, n, v] = sum_l latent_out[b, n, l] * w_uv[n, l, v]
+ *   latent_out  device, bf16, element (b, n, l) at b * x_token_stride +
+ *               n * x_head_stride + l (Lkv = 512).
+ *   w_uv        device, bf16 [N, 512, 128], contiguous.
+ *   out         device, bf16 [batch, N, 128], contiguous.
+ * Strides are in elements and must be multiples of 8, the input and weight
+ * pointers 16-byte aligned and the output 8-byte aligned, else
+ * MLA_ERR_UNSUPPORTED.  Negative sizes or strides: MLA_ERR_BAD_SHAPE.
+ * Missing pointers: MLA_ERR_NULL_POINTER.
+ */
+mla_status_t mla_absorb_query(int32_t batch, int32_t num_heads, const void *q_nope,
+                              int64_t q_token_stride, int64_t q_head_stride,
+                              const void *w_uk_t, void *ql_nope, hipStream_t stream);
+mla_status_t mla_up_project(int32_t batch, int32_t num_heads, const void *latent_out,
+                            int64_t x_token_stride, int64_t x_head_stride, const void *w_uv,
+                            void *out, hipStream_t stream);
+
+/*
  * Multi-token decode (speculative decoding with a uniform query length; vLLM
  * API docs, mla_attention, QueryLenSupport "UNIFORM": every request of the
  * batch has the same q_len > 1 new tokens; the metadata builder's causal /

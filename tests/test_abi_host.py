@@ -125,3 +125,15 @@ def test_insert_arguments(lib):
     assert insert(lib, dt=1) == 1                      # fp8 needs cache_scale_inv
     assert insert(lib, ql=None) == 1 and insert(lib, qp=None) == 1
     assert insert(lib, q_out=None) == 1
+
+
+def test_projection_arguments(lib):
+    for f in (lib.mla_absorb_query, lib.mla_up_project):
+        assert f(-1, 8, FAKE, 1024, 128, FAKE, FAKE, None) == 2
+        assert f(4, 8, FAKE, -8, 128, FAKE, FAKE, None) == 2
+        assert f(0, 8, None, 0, 0, None, None, None) == 0          # nothing to do
+        assert f(4, 8, None, 1024, 128, FAKE, FAKE, None) == 1
+        assert f(4, 8, FAKE, 1024, 128, None, FAKE, None) == 1
+        assert f(4, 8, FAKE, 1024, 128, FAKE, None, None) == 1
+        assert f(4, 8, FAKE, 1023, 128, FAKE, FAKE, None) == 3     # stride not a multiple of 8
+        assert f(4, 8, ctypes.c_void_p(0x1008), 1024, 128, FAKE, FAKE, None) == 3  # alignment
