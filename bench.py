@@ -73,12 +73,9 @@ def split_kernel_bytes(wl) -> int:
 
 def split_kernel_name(wl) -> str:
     """Symbol prefix of the split kernel (the dominant one) the library
-    launches for this workload: bf16 cache with N a multiple of 64: the
-    role-split kernel; fp8 cache: the wide kernel; otherwise the 16-head
-    kernel."""
-    if wl.N % 64 == 0:
-        return "mla_split_wide" if wl.cache_dtype == "fp8_e4m3fn" else "mla_split_ws"
-    return "mla_split_h16"
+    launches for this workload: N a multiple of 64: the role-split kernel
+    (bf16 or fp8 cache); otherwise the 16-head kernel."""
+    return "mla_split_ws" if wl.N % 64 == 0 else "mla_split_h16"
 
 
 def source_hash() -> str:

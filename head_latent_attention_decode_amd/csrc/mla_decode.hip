@@ -257,45 +257,12 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned v)
 }
 
 // ===========================================================================
-// Wide kernel: 32 * NG heads per workgroup, 2 * NG waves, 32-token tiles
-// shared by all waves through an LDS ring (NG = 2: 4 waves, one per SIMD,
-// 64 heads; NG = 4: 8 waves, two per SIMD, 128 heads).
-//   wave w = (g, c), g = w / 2 picks a group of 32 heads, c = w % 2 a half.
-//   QK^T: the wave scores heads 32g + 16c .. +16 over all 32 tokens
-//         (v_mfma_f32_16x16x32_bf16, S^T = K . Q^T, 72 VGPRs of query).
-//   PV:   the wave accumulates all 32 heads of group g over output columns
-//         256c .. 256c+255 (v_mfma_f32_32x32x16_bf16, O^T = V^T . P^T, 128
-//         accumulator registers).
-// The two waves of a group exchange their bf16 probabilities and rescale
-// factors through LDS, so each K fragment read from LDS serves 16 heads and
-// each V fragment 32 heads, while a wave keeps only 16 heads of query and
-// half of the output columns in registers.
-// bf16 cache: a 4-stage ring of bf16 tiles filled by direct-to-LDS loads.
-// fp8 cache: 3 staging buffers of fp8 tiles (direct-to-LDS loads) and 2 bf16
-// stages the workgroup converts them into, one tile ahead of the compute.
+// 32-token tiles of bf16 rows, swizzled as above, and the probability rows
+// [head][token] the split kernels exchange through LDS.
 // ===========================================================================
 constexpr int kT32 = 32;                        // tokens per tile
 constexpr int kStage32 = kT32 * kRowBytes;      // 36864 bytes (bf16 tile)
-constexpr int kStage8 = kT32 * kRowBytes8;      // 18432 bytes (fp8 tile)
 constexpr int kPbufRow = 80;                    // bytes per head row (64 + 16 pad)
-constexpr int kGroupPbuf = 32 * kPbufRow;       // [head][token] bf16 per group
-
-template <int NG, bool kFp8>
-struct WideCfg {
-    static constexpr int kWaves = 2 * NG;
-    static constexpr int kThreads = 64 * kWaves;
-    // DMA instructions (64 lanes x 16 bytes) per tile, spread over the waves:
-    // wave w issues instructions w, w + kWaves, ...
-    static constexpr int kDma = kFp8 ? kStage8 / 1024 : kStage32 / 1024;   // 18 or 36
-    static constexpr int kDmaLo = kDma / kWaves;           // per wave, rounded down
-    static constexpr int kDmaHiWaves = kDma % kWaves;      // waves issuing one more
-    static constexpr int kBf16Stages = kFp8 ? 2 : 4;
-    static constexpr int kStaging = kBf16Stages * kStage32;          // fp8 staging offset
-    static constexpr int kPbuf = kStaging + (kFp8 ? 3 * kStage8 : 0);
-    static constexpr int kAbuf = kPbuf + NG * kGroupPbuf;
-    static constexpr int kLds = kAbuf + NG * 32 * 4;
-    static_assert(kLds <= 160 * 1024, "LDS budget");
-};
 
 // Wait until this wave has at most `k` tiles (k = 0, 1, 2) of loads in flight.
 template <int n>
@@ -304,7 +271,7 @@ __device__ __forceinline__ void wait_k_tiles(int k)
     if (k >= 2) wait_vmcnt<2 * n>(); else if (k == 1) wait_vmcnt<n>(); else wait_vmcnt<0>();
 }
 template <class Cfg>
-__device__ __forceinline__ void wait_tiles_wide(int w, int k)
+__device__ __forceinline__ void wait_tiles_dma(int w, int k)
 {
     if (Cfg::kDmaHiWaves != 0 && w < Cfg::kDmaHiWaves)
         wait_k_tiles<Cfg::kDmaLo + 1>(k);
@@ -312,11 +279,13 @@ __device__ __forceinline__ void wait_tiles_wide(int w, int k)
         wait_k_tiles<Cfg::kDmaLo>(k);
 }
 
-// bf16 tile: instruction i fills LDS chunks [64i, 64i+64) of the tile, i.e.
+// bf16 tile by direct-to-LDS loads, any tile (rows past t_end repeat row
+// t_end - 1): instruction i fills LDS chunks [64i, 64i+64) of the tile, i.e.
 // rows of the half h = i / 18 (rows 16h .. 16h+15), which lie in one page.
-// Logical chunk c of row r is stored at chunk c ^ swz(r).
+// Logical chunk c of row r is stored at chunk c ^ swz(r).  Cfg::kWaves waves
+// share the 36 instructions: wave w issues w, w + kWaves, ...
 template <class Cfg>
-__device__ __forceinline__ void issue_tile_wide(const Params &p, PageWindow &win,
+__device__ __forceinline__ void issue_tile_dma(const Params &p, PageWindow &win,
                                                 LDS_AS uint8_t *stage, int w, int lane, int b,
                                                 int tile_start, int t_end)
 {
@@ -344,376 +313,9 @@ __device__ __forceinline__ void issue_tile_wide(const Params &p, PageWindow &win
     }
 }
 
-// fp8 tile: 18 DMA instructions into an unswizzled staging buffer of 576-byte
-// rows; instruction i covers rows of the half i / 9.
-template <class Cfg>
-__device__ __forceinline__ void issue_tile_wide_fp8(const Params &p, PageWindow &win,
-                                                    LDS_AS uint8_t *stg, int w, int lane, int b,
-                                                    int tile_start, int t_end)
-{
-    const int last = t_end - 1;
-    const int pmask = (1 << p.page_shift) - 1;
-    const uint8_t *base[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int first = tile_start + 16 * h;
-        first = first < last ? first : last;
-        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
-    }
-#pragma unroll
-    for (int m = 0; m < (18 + Cfg::kWaves - 1) / Cfg::kWaves; ++m) {
-        const int i = w + Cfg::kWaves * m;
-        if (i < 18) {
-            const int q = i * 64 + lane;
-            const int r = q / kRowChunks8;
-            int tok = tile_start + r;
-            tok = tok < last ? tok : last;
-            dma16(base[i / 9] + (long long)(tok & pmask) * kRowBytes8 + (q % kRowChunks8) * 16,
-                  stg + i * 1024);
-        }
-    }
-}
-
-// Widen a staged fp8 tile into a swizzled bf16 stage: 4608 groups of 4 bytes
-// spread over the workgroup's threads.
-template <class Cfg>
-__device__ __forceinline__ void convert_tile_wide(const LDS_AS uint8_t *stg, LDS_AS uint8_t *stage,
-                                                  int tid)
-{
-#pragma unroll 3
-    for (int m = 0; m < 4608 / Cfg::kThreads; ++m) {
-        const int e = m * Cfg::kThreads + tid;
-        const int r = e / 144, c4 = e % 144;
-        const unsigned v = *(const LDS_AS unsigned *)(stg + r * kRowBytes8 + c4 * 4);
-        *(LDS_AS u32x2 *)(stage + r * kRowBytes + ((c4 >> 1) ^ swz(r)) * 16 + (c4 & 1) * 8) =
-            e4m3x4_to_bf16x4(v);
-    }
-}
-
-struct StateWide {
-    f32x16 o[8];      // O^T: 8 blocks of 32 output columns x 32 heads
-    float m;          // running max (log2) of the wave's 16 QK heads
-    float l;          // this lane's share of their row sums
-};
-
-struct LaneWide {
-    int c, r16, g4, r32, g2;
-    int ko[2];        // QK A-operand offsets (k even / odd)
-    int to[2][2];     // PV transposed-read offsets [half][cb parity]
-};
-
-// One 32-token tile: scores, online softmax, probability exchange, PV.
-// Contains one workgroup barrier (after the probabilities are written).
-__device__ __forceinline__ void tile_wide(StateWide &st, const bf16x8 (&qf)[18],
-                                          const LDS_AS uint8_t *stage, LDS_AS uint8_t *pbuf,
-                                          LDS_AS float *abuf, const LaneWide &ln, float scale_log2,
-                                          int tile_start, int t_end)
-{
-    // ---- S^T[token][head] for 2 blocks of 16 tokens x this wave's 16 heads.
-    // Fragment j = 2k + tb; LDS reads run kQkAhead fragments ahead of the
-    // MFMAs that consume them (one LDS read per MFMA).
-    constexpr int kQkAhead = 4;
-    auto kfrag = [&](int j) {
-        const int k = j >> 1, tb = j & 1;
-        return *(const LDS_AS bf16x8 *)(stage + ln.ko[k & 1] + (k >> 1) * 128 +
-                                        tb * 16 * kRowBytes);
-    };
-    // Four accumulator chains (token block x parity of k) keep consecutive
-    // MFMAs independent; they are summed after the loop.
-    f32x4 sc4[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-    bf16x8 kb[kQkAhead];
-#pragma unroll
-    for (int j = 0; j < kQkAhead; ++j)
-        kb[j] = kfrag(j);
-    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);   // the first reads
-#pragma unroll
-    for (int j = 0; j < 36; ++j) {
-        const bf16x8 a = kb[j % kQkAhead];
-        if (j + kQkAhead < 36)
-            kb[j % kQkAhead] = kfrag(j + kQkAhead);
-        sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j >> 1], sc4[j & 3], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA j
-        if (j + kQkAhead < 36)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read j + kQkAhead
-    }
-    // j & 3 = tb + 2 * (k & 1): chains 0, 2 hold token block 0, chains 1, 3 block 1
-    const f32x4 sc[2] = {sc4[0] + sc4[2], sc4[1] + sc4[3]};
-    // ---- mask, scale, lazy online softmax of the wave's 16 heads
-    float x[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = tile_start + 16 * tb + 4 * ln.g4 + i;
-            const float v = sc[tb][i] * scale_log2;
-            x[4 * tb + i] = tok < t_end ? v : -INFINITY;
-            mx = fmaxf(mx, x[4 * tb + i]);
-        }
-    float alpha = 1.0f;
-    if (wave_any(mx > st.m + kLazyRescale)) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(st.m, mx);
-        alpha = __builtin_amdgcn_exp2f(st.m - mnew);
-        st.m = mnew;
-        st.l *= alpha;
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const bf16x2 p01 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb] - st.m),
-                                     __builtin_amdgcn_exp2f(x[4 * tb + 1] - st.m));
-        const bf16x2 p23 = to_bf16x2(__builtin_amdgcn_exp2f(x[4 * tb + 2] - st.m),
-                                     __builtin_amdgcn_exp2f(x[4 * tb + 3] - st.m));
-        lsum += ((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]);
-        // P[head 16c + r16][tokens 16tb + 4g4 .. +4]
-        *(LDS_AS bf16x4 *)(pbuf + (16 * ln.c + ln.r16) * kPbufRow + (16 * tb + 4 * ln.g4) * 2) =
-            bf16x4{p01[0], p01[1], p23[0], p23[1]};
-    }
-    st.l += lsum;
-    if (ln.g4 == 0)
-        abuf[16 * ln.c + ln.r16] = alpha;
-    barrier_no_fence();
-
-    // ---- PV: O^T[col][head] += V^T . P^T for the group's 32 heads
-    const float al = abuf[ln.r32];
-    if (wave_any(al != 1.0f)) {
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-            st.o[cb] *= al;
-    }
-    bf16x8 pf[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        pf[kk] = *(const LDS_AS bf16x8 *)(pbuf + ln.r32 * kPbufRow + (16 * kk + 8 * ln.g2) * 2);
-    // V^T fragment j = cb + 8kk: two transposed reads; kept kPvAhead
-    // fragments ahead of the MFMAs.  Consecutive MFMAs go to different
-    // accumulators (the two k-steps of a column block are 8 MFMAs apart).
-    constexpr int kPvAhead = 3;
-    auto vfrag = [&](int j) {
-        const int cb = j & 7, kk = j >> 3;
-        const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(stage + ln.to[0][cb & 1] + off));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(stage + ln.to[1][cb & 1] + off));
-        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    bf16x8 vb[kPvAhead];
-#pragma unroll
-    for (int j = 0; j < kPvAhead; ++j)
-        vb[j] = vfrag(j);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead + 2, 0);  // P^T + first V^T
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const bf16x8 a = vb[j % kPvAhead];
-        if (j + kPvAhead < 16)
-            vb[j % kPvAhead] = vfrag(j + kPvAhead);
-        st.o[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j >> 3], st.o[j & 7], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA j
-        if (j + kPvAhead < 16)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of j + kPvAhead
-    }
-}
-
-template <int NG, bool kDirect, bool kFp8>
-__global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
-{
-    using Cfg = WideCfg<NG, kFp8>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::kLds];
-
-    int bq, s, hg;
-    decode_work(p, bq, s, hg);
-    const int b = bq / p.QL;    // the request whose pages are read
-    int t_begin, t_end;
-    chunk_range(p, bq, s, t_begin, t_end);
-
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = w >> 1;
-    LaneWide ln;
-    ln.c = w & 1;
-    ln.r16 = lane & 15;
-    ln.g4 = lane >> 4;
-    ln.r32 = lane & 31;
-    ln.g2 = lane >> 5;
-    const int HB = 32 * NG;                                       // heads per workgroup
-    const long long head0 = (long long)bq * p.N + hg * HB;       // row of head 0
-    const long long qrow = head0 + 32 * g + 16 * ln.c + ln.r16;   // QK head
-    const long long orow = head0 + 32 * g + ln.r32;               // PV head
-
-    if (t_begin >= t_end) {
-        // empty split: lse = -inf (its partial output is never read), or out = 0
-        // and lse = -inf when direct.
-        // Each thread clears 512 * HB / kThreads = 128 columns of one head.
-        const int hh = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 128;
-        if (kDirect) {
-            __bf16 *o = p.out + (head0 + hh) * kDV + c0;
-            for (int cc = 0; cc < 128; cc += 8)
-                *(bf16x8 *)(o + cc) = bf16x8{};
-            if (p.lse && (threadIdx.x & 3) == 0)
-                p.lse[head0 + hh] = -INFINITY;
-        } else if ((threadIdx.x & 3) == 0) {
-            p.part_lse[(head0 + hh) * p.S + s] = -INFINITY;
-        }
-        return;
-    }
-
-    LDS_AS uint8_t *lds = AS3(smem);
-    LDS_AS uint8_t *pbuf = lds + Cfg::kPbuf + g * kGroupPbuf;
-    LDS_AS float *abuf = (LDS_AS float *)(lds + Cfg::kAbuf) + g * 32;
-
-    // QK A operand: row 16tb + r16, logical chunk 4k + g4
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-        ln.ko[e] = ln.r16 * kRowBytes + ((4 * e) ^ ln.g4 ^ swz(ln.r16)) * 16;
-    // PV A operand (transposed reads): 16-lane group G reads token rows
-    // 16kk + 8*g2 + 4h + (j >> 2) and columns 256c + 32cb + 16(G & 1) + 4(j & 3)
-    {
-        const int G = lane >> 4, j = lane & 15;
-        const int cl = 2 * (G & 1) + ((j >> 1) & 1);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int rr = 4 * h + (j >> 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                ln.to[h][e] = (8 * ln.g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 +
-                              8 * (j & 1) + 512 * ln.c;
-        }
-    }
-
-    float scale_log2 = p.scale_log2;
-    float out_scale = 1.0f;
-    if (kFp8) {
-        const float ks = load_uniform(p.cache_scale, 0);
-        scale_log2 *= ks;
-        out_scale = ks;
-    }
-
-    // query fragments (B operand of QK): head qrow, columns 32k + 8*g4 .. +8.
-    // Completed before any tile load is issued, so every later vmcnt wait
-    // counts tile loads only.
-    bf16x8 qf[18];
-    {
-        const __bf16 *qp = p.q + qrow * kD + ln.g4 * 8;
-#pragma unroll
-        for (int k = 0; k < 18; ++k)
-            qf[k] = *(const bf16x8 *)(qp + 32 * k);
-    }
-    PageWindow win;
-    window_fill(p, win, b, t_begin >> p.page_shift, lane);
-    wait_vmcnt<0>();
-
-    StateWide st;
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-        st.o[cb] = f32x16{};
-    st.m = -INFINITY;
-    st.l = 0.f;
-
-    const int ntiles = (t_end - t_begin + kT32 - 1) / kT32;
-    if (!kFp8) {
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-            if (t < ntiles)
-                issue_tile_wide<Cfg>(p, win, lds + t * kStage32, w, lane, b, t_begin + t * kT32, t_end);
-        for (int t = 0; t < ntiles; ++t) {
-            // Wait for this wave's loads of tile t (t+1, t+2 may stay in
-            // flight); the barrier then makes every wave's loads visible and
-            // guarantees stage (t+3)%4 = (t-1)%4 and the probability buffer
-            // are no longer read.
-            const int after = ntiles - 1 - t;
-            wait_tiles_wide<Cfg>(w, after < 2 ? after : 2);
-            barrier_no_fence();
-            if (t + 3 < ntiles)
-                issue_tile_wide<Cfg>(p, win, lds + ((t + 3) & 3) * kStage32, w, lane, b,
-                                     t_begin + (t + 3) * kT32, t_end);
-            tile_wide(st, qf, lds + (t & 3) * kStage32, pbuf, abuf, ln, scale_log2,
-                      t_begin + t * kT32, t_end);
-        }
-    } else {
-        LDS_AS uint8_t *stg = lds + Cfg::kStaging;
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-            if (t < ntiles)
-                issue_tile_wide_fp8<Cfg>(p, win, stg + t * kStage8, w, lane, b, t_begin + t * kT32,
-                                         t_end);
-        wait_tiles_wide<Cfg>(w, ntiles - 1 < 2 ? ntiles - 1 : 2);
-        barrier_no_fence();
-        convert_tile_wide<Cfg>(stg, lds, tid);
-        barrier_no_fence();
-        if (3 < ntiles)
-            issue_tile_wide_fp8<Cfg>(p, win, stg, w, lane, b, t_begin + 3 * kT32, t_end);
-        for (int t = 0; t < ntiles; ++t) {
-            if (t + 1 < ntiles) {
-                // fp8 tile t+1 -> bf16 stage (t+1)%2; tiles t+2, t+3 may stay
-                // in flight.  The first barrier also retires tile t-1's use of
-                // that stage; the second retires the staging buffer, which is
-                // refilled with tile t+4.
-                const int after = ntiles - 2 - t;
-                wait_tiles_wide<Cfg>(w, after < 2 ? after : 2);
-                barrier_no_fence();
-                convert_tile_wide<Cfg>(stg + ((t + 1) % 3) * kStage8,
-                                       lds + ((t + 1) & 1) * kStage32, tid);
-                barrier_no_fence();
-                if (t + 4 < ntiles)
-                    issue_tile_wide_fp8<Cfg>(p, win, stg + ((t + 1) % 3) * kStage8, w, lane, b,
-                                             t_begin + (t + 4) * kT32, t_end);
-            }
-            tile_wide(st, qf, lds + (t & 1) * kStage32, pbuf, abuf, ln, scale_log2,
-                      t_begin + t * kT32, t_end);
-        }
-    }
-
-    // ---- epilogue: exchange (m, l) of the QK heads, normalise, write
-    float ltot = st.l + __shfl_xor(st.l, 16);
-    ltot += __shfl_xor(ltot, 32);
-    barrier_no_fence();   // every wave is done with pbuf / abuf
-    LDS_AS float *mbuf = (LDS_AS float *)(lds + Cfg::kPbuf) + g * 64;
-    if (ln.g4 == 0) {
-        mbuf[16 * ln.c + ln.r16] = st.m;
-        mbuf[32 + 16 * ln.c + ln.r16] = ltot;
-    }
-    barrier_no_fence();
-    const float mh = mbuf[ln.r32];
-    const float lh = mbuf[32 + ln.r32];
-    const float inv = out_scale / lh;
-    const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
-    const int g2 = ln.g2;
-    if (kDirect) {
-        __bf16 *o = p.out + orow * kDV + 256 * ln.c;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int col = cb * 32 + q4 * 8 + g2 * 4;
-                const bf16x2 v0 = to_bf16x2(st.o[cb][4 * q4] * inv, st.o[cb][4 * q4 + 1] * inv);
-                const bf16x2 v1 = to_bf16x2(st.o[cb][4 * q4 + 2] * inv, st.o[cb][4 * q4 + 3] * inv);
-                *(bf16x4 *)(o + col) = bf16x4{v0[0], v0[1], v1[0], v1[1]};
-            }
-        if (p.lse && ln.c == 0 && g2 == 0)
-            p.lse[orow] = lse_nat;
-    } else {
-        float *o = p.part_out + (orow * p.S + s) * kDV + 256 * ln.c;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int col = cb * 32 + q4 * 8 + g2 * 4;
-                *(f32x4 *)(o + col) = f32x4{st.o[cb][4 * q4] * inv, st.o[cb][4 * q4 + 1] * inv,
-                                            st.o[cb][4 * q4 + 2] * inv, st.o[cb][4 * q4 + 3] * inv};
-            }
-        if (ln.c == 0 && g2 == 0)
-            p.part_lse[orow * p.S + s] = lse_nat;
-    }
-}
-
 // ===========================================================================
-// Role-split kernel (bf16 cache, N a multiple of 64): 64 heads per
-// workgroup, 8 waves, two per SIMD.
+// Role-split kernel (N a multiple of 64): 64 heads per workgroup, 8 waves,
+// two per SIMD.
 //   score waves 0..3: wave q scores heads 16q .. 16q+15 (QK^T on
 //     v_mfma_f32_16x16x32_bf16 as S^T = K . Q^T, 72 VGPRs of query) and runs
 //     the online softmax; it writes bf16 probabilities P[head][token] and the
@@ -725,8 +327,14 @@ __global__ __launch_bounds__(64 * 2 * NG, 1) void mla_split_wide(Params p)
 // Iteration i of the main loop holds one barrier; after it the score waves
 // work on tile i while the value waves work on tile i-1, so on every SIMD the
 // softmax and LDS traffic of one wave overlap the MFMAs of the other.  Tiles
-// are 32 tokens in a 4-stage LDS ring filled by direct-to-LDS loads two tiles
-// ahead (stage (i+2)%4 was last read by the value waves in iteration i-1).
+// are 32 tokens of bf16 rows in a 4-stage LDS ring.
+//   bf16 cache: direct-to-LDS loads two tiles ahead (stage (i+2)%4 was last
+//     read by the value waves in iteration i-1).
+//   fp8 cache: the value waves load E4M3 bytes into registers three tiles
+//     ahead and, in iteration i, widen tile i+2 to bf16 and write it into
+//     stage (i+2)%4; each code is converted once, and the score and value
+//     loops are those of the bf16 cache.  The per-tensor scale is folded
+//     into the softmax scale and into the final normalisation.
 // ===========================================================================
 constexpr int kWsStages = 4;
 __device__ __forceinline__ LDS_AS uint8_t *stage_of_ws(LDS_AS uint8_t *lds, int t)
@@ -795,6 +403,85 @@ __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
     for (int m = 0; m < 9; ++m) {
         const int i = v + 4 * m;
         dma16s(i < 18 ? base[0] : base[1], off[m], stage + i * 1024);
+    }
+}
+
+// fp8 cache: value wave v's share of a tile is 9 eight-byte loads per lane.
+// Load i (i = v + 4m) covers half-chunks q = 64i + lane: row r = q / 72,
+// LDS position q % 72 of the row (16 bytes of bf16), which holds logical
+// chunk c = (q % 72) ^ swz(r), i.e. the E4M3 bytes 8c .. 8c+7 of the row.
+// The offsets are relative to the first row of the load's half-tile.
+__device__ __forceinline__ void ws_load_offsets8(int v, int lane, int (&off)[9])
+{
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        const int q = i * 64 + lane;
+        const int r = q / kRowChunks;
+        const int c = (q % kRowChunks) ^ swz(r);
+        off[m] = (r - 16 * (i / 18)) * kRowBytes8 + c * 8;
+    }
+}
+
+// Loads of a whole fp8 tile into registers (compiler-tracked vector loads).
+__device__ __forceinline__ void ws_load8_full(const Params &p, PageWindow &win, int v, int lane,
+                                              int b, int tile_start, const int (&off)[9],
+                                              u32x2 (&r)[9])
+{
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int first = tile_start + 16 * h;
+        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
+        base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes8;
+    }
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        r[m] = *(const u32x2 *)((i < 18 ? base[0] : base[1]) + off[m]);
+    }
+}
+
+// The last, partial fp8 tile: rows past t_end repeat row t_end - 1 (finite
+// values whose scores are masked), so every LDS row holds a real row.
+__device__ __forceinline__ void ws_load8_part(const Params &p, PageWindow &win, int v, int lane,
+                                              int b, int tile_start, int t_end, u32x2 (&r)[9])
+{
+    const int last = t_end - 1;
+    const int pmask = (1 << p.page_shift) - 1;
+    const uint8_t *base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int first = tile_start + 16 * h;
+        first = first < last ? first : last;
+        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
+        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
+    }
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        const int q = i * 64 + lane;
+        const int rr = q / kRowChunks;
+        int tok = tile_start + rr;
+        tok = tok < last ? tok : last;
+        const int c = (q % kRowChunks) ^ swz(rr);
+        r[m] = *(const u32x2 *)((i < 18 ? base[0] : base[1]) + (long long)(tok & pmask) * kRowBytes8 +
+                                c * 8);
+    }
+}
+
+// Widen value wave v's 9 loads of a tile to bf16 and write them at their
+// swizzled positions of the stage (16 consecutive bytes per lane).
+__device__ __forceinline__ void ws_store8(LDS_AS uint8_t *stage, int v, int lane,
+                                          const u32x2 (&r)[9])
+{
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+        const int i = v + 4 * m;
+        const u32x2 lo = e4m3x4_to_bf16x4(r[m][0]);
+        const u32x2 hi = e4m3x4_to_bf16x4(r[m][1]);
+        *(LDS_AS u32x4 *)(stage + i * 1024 + lane * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 }
 
@@ -924,7 +611,7 @@ __device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], const LDS_AS ui
     }
 }
 
-template <bool kDirect>
+template <bool kDirect, bool kFp8>
 __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsLds];
@@ -961,6 +648,13 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     LDS_AS float *mbuf = (LDS_AS float *)(lds + kWsMbuf);
 
     const int ntiles = (t_end - t_begin + kT32 - 1) / kT32;
+    float scale_log2 = p.scale_log2;
+    float out_scale = 1.0f;
+    if (kFp8) {
+        const float ks = load_uniform(p.cache_scale, 0);
+        scale_log2 *= ks;
+        out_scale = ks;
+    }
     // Each role runs its own copy of the loop (same barriers), so the query
     // registers of the score waves and the accumulators of the value waves
     // are never live at the same time.  Iteration i: after the barrier the
@@ -991,11 +685,11 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
                 if (ts + kT32 <= t_end)
                     ws_score_tile<false>(m, l, qf, lds + (i & 3) * kStage32,
                                          prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                         g4, p.scale_log2, ts, t_end);
+                                         g4, scale_log2, ts, t_end);
                 else
                     ws_score_tile<true>(m, l, qf, lds + (i & 3) * kStage32,
                                         prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                        g4, p.scale_log2, ts, t_end);
+                                        g4, scale_log2, ts, t_end);
             }
             if (i == ntiles - 1) {
                 // final (m, l) of the wave's heads, read by the value waves
@@ -1032,36 +726,74 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         }
     }
     int loff[9];
-    ws_load_offsets(vq, lane, loff);
+    if (kFp8)
+        ws_load_offsets8(vq, lane, loff);
+    else
+        ws_load_offsets(vq, lane, loff);
     PageWindow win;
     window_fill(p, win, b, t_begin >> p.page_shift, lane);
     wait_vmcnt<0>();
-    auto issue = [&](int t) {
-        const int ts = t_begin + t * kT32;
-        LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
-        if (ts + kT32 <= t_end)
-            ws_issue_full(p, win, stage, vq, lane, b, ts, loff);
-        else
-            issue_tile_wide<WsDma>(p, win, stage, vq, lane, b, ts, t_end);
-    };
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        if (t < ntiles)
-            issue(t);
     f32x16 o[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
         o[cb][0] = o[cb][1] = f32x16{};
-    for (int i = 0; i <= ntiles; ++i) {
-        if (i < ntiles)
-            wait_tiles_wide<WsDma>(vq, i + 1 < ntiles ? 1 : 0);
-        barrier_no_fence();
-        if (i + 2 < ntiles)
-            issue(i + 2);
+    auto value = [&](int i) {
         if (i > 0) {
             const int j = i - 1;
             ws_value_tile(o, lds + (j & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
                           abuf + (j & 1) * 64, to, r32, g2);
+        }
+    };
+    if (!kFp8) {
+        auto issue = [&](int t) {
+            const int ts = t_begin + t * kT32;
+            LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
+            if (ts + kT32 <= t_end)
+                ws_issue_full(p, win, stage, vq, lane, b, ts, loff);
+            else
+                issue_tile_dma<WsDma>(p, win, stage, vq, lane, b, ts, t_end);
+        };
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            if (t < ntiles)
+                issue(t);
+        for (int i = 0; i <= ntiles; ++i) {
+            if (i < ntiles)
+                wait_tiles_dma<WsDma>(vq, i + 1 < ntiles ? 1 : 0);
+            barrier_no_fence();
+            if (i + 2 < ntiles)
+                issue(i + 2);
+            value(i);
+        }
+    } else {
+        // One register set.  Tiles are written two ahead: in iteration i,
+        // after the PV of tile i-1 has been issued, the set holds tile i+2
+        // (loaded in iteration i-1), which goes to stage (i+2)%4 (last read
+        // in iteration i-1), and is refilled with tile i+3.
+        u32x2 rg[9];
+        auto load = [&](int t) {
+            const int ts = t_begin + t * kT32;
+            if (ts + kT32 <= t_end)
+                ws_load8_full(p, win, vq, lane, b, ts, loff, rg);
+            else
+                ws_load8_part(p, win, vq, lane, b, ts, t_end, rg);
+        };
+        load(0);
+        ws_store8(lds, vq, lane, rg);
+        if (1 < ntiles) {
+            load(1);
+            ws_store8(lds + kStage32, vq, lane, rg);
+        }
+        if (2 < ntiles)
+            load(2);
+        for (int i = 0; i <= ntiles; ++i) {
+            barrier_no_fence();
+            value(i);
+            if (i + 2 < ntiles) {
+                ws_store8(lds + ((i + 2) & 3) * kStage32, vq, lane, rg);
+                if (i + 3 < ntiles)
+                    load(i + 3);
+            }
         }
     }
 
@@ -1081,7 +813,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         const int hh = 32 * hb + r32;
         const float mh = mbuf[hh];
         const float lh = mbuf[64 + hh];
-        const float inv = 1.0f / lh;
+        const float inv = out_scale / lh;
         // lane (r32, g2) holds head hh, columns 32cb + 8q4 + 4g2 .. +4
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -1919,37 +1651,23 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     const bool direct = part_out == nullptr;
     const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
     // Kernel choice by head count and cache dtype:
-    //   bf16, N % 64 == 0:   role-split kernel, 64 heads per workgroup
-    //   fp8,  N % 128 == 0:  wide kernel, 128 heads per workgroup
-    //   fp8,  N % 64 == 0:   wide kernel, 64 heads per workgroup
-    //   otherwise:           16 heads per workgroup
-    int heads_per_wg = 16;
-    if (!fp8 && s->num_heads % 64 == 0)
-        heads_per_wg = 64;
-    else if (fp8 && s->num_heads % 128 == 0)
-        heads_per_wg = 128;
-    else if (fp8 && s->num_heads % 64 == 0)
-        heads_per_wg = 64;
+    //   N % 64 == 0:   role-split kernel, 64 heads per workgroup
+    //   otherwise:     16 heads per workgroup
+    const int heads_per_wg = s->num_heads % 64 == 0 ? 64 : 16;
     p.HG = s->num_heads / heads_per_wg;
     const long long grid = (long long)s->batch * q_len * S * p.HG;
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
     const dim3 g((unsigned)grid);
-    if (!fp8 && heads_per_wg == 64) {
-        if (direct)
-            hipLaunchKernelGGL(mla_split_ws<true>, g, dim3(512), 0, stream, p);
+    if (heads_per_wg == 64) {
+        if (direct && fp8)
+            hipLaunchKernelGGL((mla_split_ws<true, true>), g, dim3(512), 0, stream, p);
+        else if (fp8)
+            hipLaunchKernelGGL((mla_split_ws<false, true>), g, dim3(512), 0, stream, p);
+        else if (direct)
+            hipLaunchKernelGGL((mla_split_ws<true, false>), g, dim3(512), 0, stream, p);
         else
-            hipLaunchKernelGGL(mla_split_ws<false>, g, dim3(512), 0, stream, p);
-    } else if (heads_per_wg == 128) {
-        if (direct)
-            hipLaunchKernelGGL((mla_split_wide<4, true, true>), g, dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((mla_split_wide<4, false, true>), g, dim3(512), 0, stream, p);
-    } else if (heads_per_wg == 64) {
-        if (direct)
-            hipLaunchKernelGGL((mla_split_wide<2, true, true>), g, dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((mla_split_wide<2, false, true>), g, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((mla_split_ws<false, false>), g, dim3(512), 0, stream, p);
     } else if (fp8) {
         if (direct)
             hipLaunchKernelGGL((mla_split_h16<true, true>), g, dim3(256), 0, stream, p);

@@ -41,15 +41,18 @@ def test_small_grid(N, page, S):
     G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what=f"N={N} P={page} S={S}")
 
 
-@pytest.mark.parametrize("N", [16, 128])
+@pytest.mark.parametrize("N", [16, 64, 128])
+@pytest.mark.parametrize("page", [16, 64])
 @pytest.mark.parametrize("S", [1, 2, 5])
-def test_fp8_small(N, S):
-    lens = [1, 40, 64, 65, 300, 777]
-    wl = W.make_workload(len(lens), N, 64, lens, seed=200 + N + S, cache_dtype="fp8_e4m3fn")
-    _say("fp8 case", N, S)
+def test_fp8_small(N, page, S):
+    # 2100 tokens at 16-token pages cross the 64-page window of the tile loader
+    lens = [1, 40, 64, 65, 300, 777, 2100]
+    wl = W.make_workload(len(lens), N, page, lens, seed=200 + N + page + S,
+                         cache_dtype="fp8_e4m3fn")
+    _say("fp8 case", N, page, S)
     out, lse = G.run(wl, S)
     ref_o, ref_l = G.reference(wl)
-    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn", what=f"fp8 N={N} S={S}")
+    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn", what=f"fp8 N={N} P={page} S={S}")
 
 
 @pytest.mark.parametrize("N", [16, 128])
