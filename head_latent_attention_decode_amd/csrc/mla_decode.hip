@@ -348,13 +348,22 @@ constexpr int kWsMbuf = kWsAbuf + 2 * 64 * 4;                    // m [64], l [6
 constexpr int kWsLds = kWsMbuf + 2 * 64 * 4;
 static_assert(kWsLds <= 160 * 1024, "LDS budget");
 
-// Tile loads are issued by the 4 value waves only: value wave v issues
-// instructions i = v + 4m (m < 9) of the 36 that fill a 32-token tile.
+// Who loads the tiles (each load instruction stalls its wave for tens of
+// cycles, so where they go was set by measurement):
+//   bf16: the 4 value waves, right after the barrier: value wave v issues the
+//     direct-to-LDS instructions i = v + 4m (m < 9) of the 36 that fill a
+//     tile (16 bytes per lane).  Giving the score waves a share made every
+//     placement slower.
+//   fp8: all 8 waves: wave w issues the loads i = w + 8m of the 18 that
+//     carry a tile (16 E4M3 bytes per lane), 3 for waves 0 and 1 and 2 for
+//     the others; score waves right after the barrier, value waves after
+//     their PV MFMAs.
 struct WsDma {
     static constexpr int kWaves = 4;
     static constexpr int kDmaLo = 9;
     static constexpr int kDmaHiWaves = 0;
 };
+constexpr int kWsLd8Max = 3;       // fp8 loads per wave and tile, at most
 
 // One direct-to-LDS load with a wave-uniform 64-bit base in SGPRs and a
 // 32-bit per-lane byte offset (the saddr form: no per-lane 64-bit address
@@ -368,12 +377,12 @@ __device__ __forceinline__ void dma16s(const uint8_t *sbase, int voff, LDS_AS vo
                  : "memory", "m0");
 }
 
-// Per-lane source offsets of value wave v's 9 load instructions, relative to
-// the first row of the instruction's half-tile; they do not depend on the
-// tile.  Instruction i fills LDS chunks [64i, 64i+64): chunk q = 64i + lane
-// is row r = q / 72, stored position q % 72, which holds logical chunk
-// (q % 72) ^ swz(r) of the row.
-__device__ __forceinline__ void ws_load_offsets(int v, int lane, int (&off)[9])
+// Per-lane source offsets of value wave v's 9 bf16 load instructions,
+// relative to the first row of the instruction's half-tile; they do not
+// depend on the tile.  Instruction i fills LDS chunks [64i, 64i+64): chunk
+// q = 64i + lane is row r = q / 72, stored position q % 72, which holds
+// logical chunk (q % 72) ^ swz(r) of the row.
+__device__ __forceinline__ void ws_dma_offsets(int v, int lane, int (&off)[9])
 {
 #pragma unroll
     for (int m = 0; m < 9; ++m) {
@@ -385,8 +394,8 @@ __device__ __forceinline__ void ws_load_offsets(int v, int lane, int (&off)[9])
     }
 }
 
-// A whole tile (tile_start + 32 <= t_end): two scalar half-tile bases, then
-// 9 loads with the precomputed offsets.
+// A whole bf16 tile (tile_start + 32 <= t_end): two scalar half-tile bases,
+// then value wave v's 9 loads with the precomputed offsets.
 __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
                                               LDS_AS uint8_t *stage, int v, int lane, int b,
                                               int tile_start, const int (&off)[9])
@@ -406,84 +415,202 @@ __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
     }
 }
 
-// fp8 cache: value wave v's share of a tile is 9 eight-byte loads per lane.
-// Load i (i = v + 4m) covers half-chunks q = 64i + lane: row r = q / 72,
-// LDS position q % 72 of the row (16 bytes of bf16), which holds logical
-// chunk c = (q % 72) ^ swz(r), i.e. the E4M3 bytes 8c .. 8c+7 of the row.
-// The offsets are relative to the first row of the load's half-tile.
-__device__ __forceinline__ void ws_load_offsets8(int v, int lane, int (&off)[9])
+// fp8 cache.  Load i covers 16-byte pieces q = 64i + lane: row r = q / 36,
+// E4M3 bytes 16c .. 16c+15 (c = q % 36), i.e. the bf16 logical chunks 2c and
+// 2c+1 of the row, stored at positions (2c) ^ swz(r) and that ^ 1.  Source
+// offsets are relative to the first row of the load's half-tile (i / 9);
+// destination offsets are relative to the stage.  Every wave issues
+// kWsLd8Max loads, so that no register is loaded on one path only (the
+// compiler would then copy it, and wait for the load, at the loop's end): a
+// wave whose third load index passes 17 repeats its first load and does not
+// write it.
+__device__ __forceinline__ int ws_ld8_index(int w, int m)
+{
+    const int i = w + 8 * m;
+    return i < 18 ? i : w;
+}
+__device__ __forceinline__ void ws_ld8_offsets(int w, int lane, int (&src)[kWsLd8Max],
+                                               int (&dst)[kWsLd8Max])
 {
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
+    for (int m = 0; m < kWsLd8Max; ++m) {
+        const int i = ws_ld8_index(w, m);
         const int q = i * 64 + lane;
-        const int r = q / kRowChunks;
-        const int c = (q % kRowChunks) ^ swz(r);
-        off[m] = (r - 16 * (i / 18)) * kRowBytes8 + c * 8;
+        const int r = q / 36, c = q % 36;
+        src[m] = (r - 16 * (i / 9)) * kRowBytes8 + c * 16;
+        dst[m] = r * kRowBytes + ((2 * c) ^ swz(r)) * 16;
     }
 }
 
-// Loads of a whole fp8 tile into registers (compiler-tracked vector loads).
-__device__ __forceinline__ void ws_load8_full(const Params &p, PageWindow &win, int v, int lane,
-                                              int b, int tile_start, const int (&off)[9],
-                                              u32x2 (&r)[9])
+// Raw buffer resource over the bytes from `base` (wave-uniform): the loads
+// below take a 32-bit per-lane offset against a scalar base, so no 64-bit
+// per-lane address is formed, and the compiler still tracks them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// The wave's loads of a whole fp8 tile into registers.
+__device__ __forceinline__ void ws_ld8_full(const Params &p, PageWindow &win, int w, int lane,
+                                            int b, int tile_start, const int (&src)[kWsLd8Max],
+                                            u32x4 (&r)[kWsLd8Max])
 {
     const int pmask = (1 << p.page_shift) - 1;
-    const uint8_t *base[2];
+    __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int first = tile_start + 16 * h;
         const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes8;
+        rs[h] = rows_rsrc(p.cache +
+                          (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes8);
     }
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
-        r[m] = *(const u32x2 *)((i < 18 ? base[0] : base[1]) + off[m]);
+    for (int m = 0; m < kWsLd8Max; ++m) {
+        const int i = ws_ld8_index(w, m);
+        r[m] = __builtin_amdgcn_raw_buffer_load_b128(i < 9 ? rs[0] : rs[1], src[m], 0, 0);
     }
 }
 
 // The last, partial fp8 tile: rows past t_end repeat row t_end - 1 (finite
 // values whose scores are masked), so every LDS row holds a real row.
-__device__ __forceinline__ void ws_load8_part(const Params &p, PageWindow &win, int v, int lane,
-                                              int b, int tile_start, int t_end, u32x2 (&r)[9])
+__device__ __forceinline__ void ws_ld8_part(const Params &p, PageWindow &win, int w, int lane,
+                                            int b, int tile_start, int t_end,
+                                            u32x4 (&r)[kWsLd8Max])
 {
     const int last = t_end - 1;
     const int pmask = (1 << p.page_shift) - 1;
-    const uint8_t *base[2];
+    __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         int first = tile_start + 16 * h;
         first = first < last ? first : last;
         const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes8;
+        rs[h] = rows_rsrc(p.cache + ((long long)blk << p.page_shift) * kRowBytes8);
     }
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
+    for (int m = 0; m < kWsLd8Max; ++m) {
+        const int i = ws_ld8_index(w, m);
         const int q = i * 64 + lane;
-        const int rr = q / kRowChunks;
+        const int rr = q / 36;
         int tok = tile_start + rr;
         tok = tok < last ? tok : last;
-        const int c = (q % kRowChunks) ^ swz(rr);
-        r[m] = *(const u32x2 *)((i < 18 ? base[0] : base[1]) + (long long)(tok & pmask) * kRowBytes8 +
-                                c * 8);
+        r[m] = __builtin_amdgcn_raw_buffer_load_b128(
+            i < 9 ? rs[0] : rs[1], (tok & pmask) * kRowBytes8 + (q % 36) * 16, 0, 0);
     }
 }
 
-// Widen value wave v's 9 loads of a tile to bf16 and write them at their
-// swizzled positions of the stage (16 consecutive bytes per lane).
-__device__ __forceinline__ void ws_store8(LDS_AS uint8_t *stage, int v, int lane,
-                                          const u32x2 (&r)[9])
+// Widen the wave's loads of a tile to bf16 and write them at their swizzled
+// positions of the stage: two 16-byte writes per load.
+__device__ __forceinline__ void ws_st8(LDS_AS uint8_t *stage, int w, const int (&dst)[kWsLd8Max],
+                                       const u32x4 (&r)[kWsLd8Max])
 {
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
-        const u32x2 lo = e4m3x4_to_bf16x4(r[m][0]);
-        const u32x2 hi = e4m3x4_to_bf16x4(r[m][1]);
-        *(LDS_AS u32x4 *)(stage + i * 1024 + lane * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    for (int m = 0; m < kWsLd8Max; ++m) {
+        if (w + 8 * m < 18) {
+            const u32x2 a = e4m3x4_to_bf16x4(r[m][0]);
+            const u32x2 b = e4m3x4_to_bf16x4(r[m][1]);
+            const u32x2 c = e4m3x4_to_bf16x4(r[m][2]);
+            const u32x2 d = e4m3x4_to_bf16x4(r[m][3]);
+            *(LDS_AS u32x4 *)(stage + dst[m]) = u32x4{a[0], a[1], b[0], b[1]};
+            *(LDS_AS u32x4 *)(stage + (dst[m] ^ 16)) = u32x4{c[0], c[1], d[0], d[1]};
+        }
     }
 }
+
+// All of a wave's tile traffic: its share of the loads of each tile and,
+// for an fp8 cache, the registers that carry them to the stage.  w is the
+// wave's index among the loading waves (value waves 0..3 for bf16, all
+// waves 0..7 for fp8).
+template <bool kFp8>
+struct WsLoader {
+    PageWindow win;
+    int off[kFp8 ? kWsLd8Max : 9];
+    int dst[kFp8 ? kWsLd8Max : 1];
+    u32x4 rg[kFp8 ? kWsLd8Max : 1];
+    int w, lane, b, t_begin, t_end;
+
+    __device__ __forceinline__ void init(const Params &p, int w_, int lane_, int b_, int t0,
+                                         int t1)
+    {
+        w = w_;
+        lane = lane_;
+        b = b_;
+        t_begin = t0;
+        t_end = t1;
+        if constexpr (kFp8)
+            ws_ld8_offsets(w, lane, off, dst);
+        else
+            ws_dma_offsets(w, lane, off);
+        window_fill(p, win, b, t_begin >> p.page_shift, lane);
+    }
+    // bf16: direct-to-LDS loads of tile t into its stage
+    __device__ __forceinline__ void issue(const Params &p, LDS_AS uint8_t *lds, int t)
+    {
+        const int ts = t_begin + t * kT32;
+        LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
+        if (ts + kT32 <= t_end)
+            ws_issue_full(p, win, stage, w, lane, b, ts, off);
+        else
+            issue_tile_dma<WsDma>(p, win, stage, w, lane, b, ts, t_end);
+    }
+    // bf16: wait until at most k of this wave's tiles are in flight
+    __device__ __forceinline__ void wait(int k) { wait_tiles_dma<WsDma>(w, k); }
+    // fp8: loads of tile t into the registers
+    __device__ __forceinline__ void load(const Params &p, int t)
+    {
+        const int ts = t_begin + t * kT32;
+        if (ts + kT32 <= t_end)
+            ws_ld8_full(p, win, w, lane, b, ts, off, rg);
+        else
+            ws_ld8_part(p, win, w, lane, b, ts, t_end, rg);
+    }
+    // fp8: the registers, widened, into tile t's stage
+    __device__ __forceinline__ void store(LDS_AS uint8_t *lds, int t)
+    {
+        ws_st8(lds + (t & 3) * kStage32, w, dst, rg);
+    }
+    // Before the first barrier: tiles 0 and 1 issued (bf16), or written with
+    // tile 2 in the registers (fp8).
+    __device__ __forceinline__ void prologue(const Params &p, LDS_AS uint8_t *lds, int ntiles)
+    {
+        if constexpr (kFp8) {
+            load(p, 0);
+            store(lds, 0);
+            if (1 < ntiles) {
+                load(p, 1);
+                store(lds, 1);
+            }
+            load(p, 2 < ntiles ? 2 : ntiles - 1);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (t < ntiles)
+                    issue(p, lds, t);
+        }
+    }
+    // bf16, top of iteration i: this wave's loads of tile i have landed
+    __device__ __forceinline__ void before_barrier(int i, int ntiles)
+    {
+        if constexpr (!kFp8)
+            if (i < ntiles)
+                wait(i + 1 < ntiles ? 1 : 0);
+    }
+    // The wave's tile traffic of iteration i: bf16 issues tile i+2 into stage
+    // (i+2)%4 (last read in iteration i-1); fp8 writes tile i+2 there from
+    // the registers and loads tile i+3 (past the last tile, the last tile
+    // again: the registers are loaded on every path).
+    __device__ __forceinline__ void step(const Params &p, LDS_AS uint8_t *lds, int i, int ntiles)
+    {
+        if constexpr (kFp8) {
+            if (i + 2 < ntiles)
+                store(lds, i + 2);
+            load(p, i + 3 < ntiles ? i + 3 : ntiles - 1);
+        } else {
+            if (i + 2 < ntiles)
+                issue(p, lds, i + 2);
+        }
+    }
+};
 
 // Scores of one 32-token tile for a score wave's 16 heads, lazy online
 // softmax, probabilities and rescale factor to LDS.
@@ -559,12 +686,40 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
         *arow = alpha;
 }
 
+// V^T fragment j (0..7) of a tile for a value wave: two transposed reads
+// giving tokens 16kk + 8 g2 .. +8 of column 128vq + 32cb + r32 (j = cb + 4kk),
+// the A operand of O^T = V^T . P^T for both head blocks.
+__device__ __forceinline__ bf16x8 ws_vfrag(const LDS_AS uint8_t *stage, const int (&to)[2][2],
+                                           int j)
+{
+    const int cb = j & 3, kk = j >> 2;
+    const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
+    const bf16x4 lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(stage + to[0][cb & 1] + off));
+    const bf16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(stage + to[1][cb & 1] + off));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // PV of one 32-token tile for a value wave: O^T[col][head] for its 128
-// columns (4 blocks of 32) and the 64 heads (2 blocks of 32).
-__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], const LDS_AS uint8_t *stage,
+// columns (4 blocks of 32) and the 64 heads (2 blocks of 32).  vt holds the
+// tile's V^T fragments, read during the previous iteration; as the MFMAs
+// consume them, vt is refilled with the fragments of the tile in stage
+// `next` (complete and visible since this iteration's barrier).  The
+// probabilities and rescale factors are read together, so the MFMAs wait
+// for one LDS round trip.
+__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], bf16x8 (&vt)[8],
+                                              const LDS_AS uint8_t *next,
                                               const LDS_AS uint8_t *pbuf, const LDS_AS float *abuf,
                                               const int (&to)[2][2], int r32, int g2)
 {
+    bf16x8 pf[2][2];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            pf[hb][kk] = *(const LDS_AS bf16x8 *)(pbuf + (32 * hb + r32) * kPbufRow +
+                                                  (16 * kk + 8 * g2) * 2);
     const float al0 = abuf[r32], al1 = abuf[32 + r32];
     if (wave_any(al0 != 1.0f || al1 != 1.0f)) {
 #pragma unroll
@@ -573,41 +728,15 @@ __device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], const LDS_AS ui
             o[cb][1] *= al1;
         }
     }
-    bf16x8 pf[2][2];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            pf[hb][kk] = *(const LDS_AS bf16x8 *)(pbuf + (32 * hb + r32) * kPbufRow +
-                                                  (16 * kk + 8 * g2) * 2);
-    // V^T fragment j = cb + 4kk (two transposed reads), used by the MFMAs of
-    // both head blocks; kept kAhead fragments ahead.
-    constexpr int kAhead = 2;
-    auto vfrag = [&](int j) {
-        const int cb = j & 3, kk = j >> 2;
-        const int off = kk * 16 * kRowBytes + (cb >> 1) * 128;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(stage + to[0][cb & 1] + off));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(stage + to[1][cb & 1] + off));
-        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    bf16x8 vb[kAhead];
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j)
-        vb[j] = vfrag(j);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * kAhead, 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const bf16x8 a = vb[j % kAhead];
-        if (j + kAhead < 8)
-            vb[j % kAhead] = vfrag(j + kAhead);
+        const bf16x8 a = vt[j];
+        vt[j] = ws_vfrag(next, to, j);
         const int cb = j & 3, kk = j >> 2;
         o[cb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0][kk], o[cb][0], 0, 0, 0);
         o[cb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1][kk], o[cb][1], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (j + kAhead < 8)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 }
 
@@ -677,9 +806,18 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
             ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
         LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * kPbufRow;
         LDS_AS float *arow = abuf + 16 * sq + r16;
+        // fp8: the score waves take part in the tile loads (after the query
+        // loads, which complete inside the page-window fill)
+        WsLoader<kFp8> ld;
+        if constexpr (kFp8) {
+            ld.init(p, w, lane, b, t_begin, t_end);
+            ld.prologue(p, lds, ntiles);
+        }
         float m = -INFINITY, l = 0.f;
         for (int i = 0; i <= ntiles; ++i) {
             barrier_no_fence();
+            if constexpr (kFp8)
+                ld.step(p, lds, i, ntiles);
             if (i < ntiles) {
                 const int ts = t_begin + i * kT32;
                 if (ts + kT32 <= t_end)
@@ -725,76 +863,35 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
                            8 * (j & 1) + 256 * vq;
         }
     }
-    int loff[9];
-    if (kFp8)
-        ws_load_offsets8(vq, lane, loff);
-    else
-        ws_load_offsets(vq, lane, loff);
-    PageWindow win;
-    window_fill(p, win, b, t_begin >> p.page_shift, lane);
-    wait_vmcnt<0>();
+    WsLoader<kFp8> ld;
+    ld.init(p, kFp8 ? w : vq, lane, b, t_begin, t_end);
+    ld.prologue(p, lds, ntiles);
     f32x16 o[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
         o[cb][0] = o[cb][1] = f32x16{};
-    auto value = [&](int i) {
-        if (i > 0) {
+    // iteration i: this wave's tile traffic (bf16: before, fp8: after the PV)
+    // and the PV of tile i-1 with its V^T from registers, reading tile i's
+    // V^T for the next iteration (in the last iteration, tile i-1's again:
+    // stage ntiles%4 is the epilogue's)
+    bf16x8 vt[8];
+    for (int i = 0; i <= ntiles; ++i) {
+        ld.before_barrier(i, ntiles);
+        barrier_no_fence();
+        if constexpr (!kFp8)
+            ld.step(p, lds, i, ntiles);
+        if (i == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                vt[j] = ws_vfrag(lds, to, j);
+        } else {
             const int j = i - 1;
-            ws_value_tile(o, lds + (j & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
+            const int nt = i < ntiles ? i : j;
+            ws_value_tile(o, vt, lds + (nt & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
                           abuf + (j & 1) * 64, to, r32, g2);
         }
-    };
-    if (!kFp8) {
-        auto issue = [&](int t) {
-            const int ts = t_begin + t * kT32;
-            LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
-            if (ts + kT32 <= t_end)
-                ws_issue_full(p, win, stage, vq, lane, b, ts, loff);
-            else
-                issue_tile_dma<WsDma>(p, win, stage, vq, lane, b, ts, t_end);
-        };
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            if (t < ntiles)
-                issue(t);
-        for (int i = 0; i <= ntiles; ++i) {
-            if (i < ntiles)
-                wait_tiles_dma<WsDma>(vq, i + 1 < ntiles ? 1 : 0);
-            barrier_no_fence();
-            if (i + 2 < ntiles)
-                issue(i + 2);
-            value(i);
-        }
-    } else {
-        // One register set.  Tiles are written two ahead: in iteration i,
-        // after the PV of tile i-1 has been issued, the set holds tile i+2
-        // (loaded in iteration i-1), which goes to stage (i+2)%4 (last read
-        // in iteration i-1), and is refilled with tile i+3.
-        u32x2 rg[9];
-        auto load = [&](int t) {
-            const int ts = t_begin + t * kT32;
-            if (ts + kT32 <= t_end)
-                ws_load8_full(p, win, vq, lane, b, ts, loff, rg);
-            else
-                ws_load8_part(p, win, vq, lane, b, ts, t_end, rg);
-        };
-        load(0);
-        ws_store8(lds, vq, lane, rg);
-        if (1 < ntiles) {
-            load(1);
-            ws_store8(lds + kStage32, vq, lane, rg);
-        }
-        if (2 < ntiles)
-            load(2);
-        for (int i = 0; i <= ntiles; ++i) {
-            barrier_no_fence();
-            value(i);
-            if (i + 2 < ntiles) {
-                ws_store8(lds + ((i + 2) & 3) * kStage32, vq, lane, rg);
-                if (i + 3 < ntiles)
-                    load(i + 3);
-            }
-        }
+        if constexpr (kFp8)
+            ld.step(p, lds, i, ntiles);
     }
 
     // ---- value-wave epilogue.  The accumulator layout scatters a store
