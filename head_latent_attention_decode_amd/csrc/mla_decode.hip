@@ -52,7 +52,7 @@ constexpr int kSplitUnit = 32;          // split boundaries are multiples of thi
 // Chunks are at least this long, so a short request fills only the first
 // splits and the trailing ones are empty: a chunk's fixed costs (query load,
 // partial write, its share of the merge) stay small next to its KV rows.
-constexpr int kMinChunk = 1024;
+constexpr int kMinChunk = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;    // log2 headroom before a rescale
@@ -1289,9 +1289,9 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 // LSE merge.  A state with lse = -inf carries no weight and its output is
 // not read (an empty chunk leaves it unwritten).
 //   mla_merge: one wave per row, each lane owns 8 of the 512 columns.
-//   mla_merge_wide: one workgroup per row for few rows and many states; its
-//   4 waves take every 4th state (loads batched 4 states deep) and add their
-//   sums through LDS.
+//   mla_merge_cols: for few rows and many states, 8 workgroups per row, each
+//   owning 64 of the 512 columns for all states: its 256 threads are 32 state
+//   slots x 8 column groups of 8, and the slots' sums are added through LDS.
 // ===========================================================================
 // Largest state lse of a row and the row's total lse (natural log).
 __device__ __forceinline__ void merge_total(const float *ls, int S, float &M, float &total)
@@ -1359,65 +1359,78 @@ __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_
         lse[row] = total;
 }
 
-__global__ __launch_bounds__(256) void mla_merge_wide(const float *__restrict__ part_out,
+constexpr int kMergeColBlocks = 8;     // 64-column blocks per row
+__global__ __launch_bounds__(256) void mla_merge_cols(const float *__restrict__ part_out,
                                                       const float *__restrict__ part_lse,
                                                       __bf16 *__restrict__ out,
                                                       float *__restrict__ lse, int rows, int S)
 {
-    __shared__ f32x4 red[3][64][2];
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __shared__ float red[32][65];   // [state slot][column] (+1: conflict-free column sums)
+    const int row = blockIdx.x / kMergeColBlocks, cb = blockIdx.x % kMergeColBlocks;
+    const int t = threadIdx.x, slot = t >> 3, cg = t & 7, lane = t & 63;
     const float *ls = part_lse + (long long)row * S;
-    float M, total;
-    merge_total(ls, S, M, total);
-    __bf16 *o = out + (long long)row * kDV + lane * 8;
-    if (M == -INFINITY) {
-        if (w == 0) {
-            *(bf16x8 *)o = bf16x8{};
-            if (lse && lane == 0)
-                lse[row] = -INFINITY;
-        }
+    const int c0 = cb * 64;
+    const float *po = part_out + (long long)row * S * kDV + c0 + 8 * cg;
+    // Slot k takes states k, k + 32, ...  Its first state's values are loaded
+    // before the row total is known, so that the two load latencies overlap.
+    f32x4 v0 = {}, v1 = {};
+    if (slot < S) {
+        v0 = *(const f32x4 *)(po + (long long)slot * kDV);
+        v1 = *(const f32x4 *)(po + (long long)slot * kDV + 4);
+    }
+    // the row's total lse, computed by every wave from its lanes' states
+    float m = -INFINITY;
+    for (int s = lane; s < S; s += 64)
+        m = fmaxf(m, ls[s]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        m = fmaxf(m, __shfl_xor(m, d));
+    float z = 0.f;
+    if (m != -INFINITY)
+        for (int s = lane; s < S; s += 64)
+            z += __builtin_amdgcn_exp2f((ls[s] - m) * kLog2e);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        z += __shfl_xor(z, d);
+    if (m == -INFINITY) {
+        // no live state: out = 0, lse = -inf
+        if (t < 8)
+            *(bf16x8 *)(out + (long long)row * kDV + c0 + 8 * t) = bf16x8{};
+        if (lse && cb == 0 && t == 0)
+            lse[row] = -INFINITY;
         return;
     }
-    // Every 4th state, 4 at a time with all 8 loads in flight.  A state of
-    // weight zero is loaded too (its workspace row exists) but dropped by a
-    // select, so an unwritten row cannot leak NaN into the sum.
-    f32x4 acc0 = {}, acc1 = {};
-    const float *po = part_out + (long long)row * S * kDV + lane * 8;
-    for (int s0 = w; s0 < S; s0 += 16) {
-        f32x4 v[4][2];
-        float l[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int s = s0 + 4 * u < S ? s0 + 4 * u : w;
-            l[u] = s0 + 4 * u < S ? ls[s] : -INFINITY;
-            v[u][0] = *(const f32x4 *)(po + (long long)s * kDV);
-            v[u][1] = *(const f32x4 *)(po + (long long)s * kDV + 4);
+    const float total = m + __builtin_amdgcn_logf(z) * kLn2;
+    // A state of weight zero is dropped by a select, so an unwritten row
+    // cannot leak NaN into the sum.
+    f32x4 a0 = {}, a1 = {};
+    for (int s = slot; s < S; s += 32) {
+        if (s != slot) {
+            v0 = *(const f32x4 *)(po + (long long)s * kDV);
+            v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
         }
+        const float l = ls[s];
+        const bool live = l != -INFINITY;
+        const float wgt = __builtin_amdgcn_exp2f((l - total) * kLog2e);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool live = l[u] != -INFINITY;
-            const float wgt = __builtin_amdgcn_exp2f((l[u] - total) * kLog2e);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc0[e] += live ? wgt * v[u][0][e] : 0.f;
-                acc1[e] += live ? wgt * v[u][1][e] : 0.f;
-            }
+        for (int e = 0; e < 4; ++e) {
+            a0[e] += live ? wgt * v0[e] : 0.f;
+            a1[e] += live ? wgt * v1[e] : 0.f;
         }
     }
-    if (w > 0) {
-        red[w - 1][lane][0] = acc0;
-        red[w - 1][lane][1] = acc1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        red[slot][8 * cg + e] = a0[e];
+        red[slot][8 * cg + 4 + e] = a1[e];
     }
     __syncthreads();
-    if (w == 0) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            acc0 += red[k][lane][0];
-            acc1 += red[k][lane][1];
-        }
-        *(bf16x8 *)o = to_bf16x8(acc0, acc1);
-        if (lse && lane == 0)
+    if (t < 64) {
+        float sum = 0.f;
+#pragma unroll 8
+        for (int k = 0; k < 32; ++k)
+            sum += red[k][t];
+        out[(long long)row * kDV + c0 + t] = (__bf16)sum;
+        if (lse && cb == 0 && t == 0)
             lse[row] = total;
     }
 }
@@ -1785,10 +1798,10 @@ mla_status_t launch_merge(int rows, int S, const float *part_out, const float *p
     if (rows == 0)
         return MLA_OK;
     // one wave per row fills the GPU once there are a few thousand rows;
-    // below that, and with enough states per row, a workgroup per row
+    // below that, and with enough states per row, 8 workgroups per row
     if (rows < 4096 && S >= 8) {
-        hipLaunchKernelGGL(mla_merge_wide, dim3((unsigned)rows), dim3(256), 0, stream, part_out,
-                           part_lse, (__bf16 *)out, lse, rows, S);
+        hipLaunchKernelGGL(mla_merge_cols, dim3((unsigned)rows * kMergeColBlocks), dim3(256), 0,
+                           stream, part_out, part_lse, (__bf16 *)out, lse, rows, S);
     } else {
         dim3 g((unsigned)((rows + 3) / 4)), blk(256);
         hipLaunchKernelGGL(mla_merge, g, blk, 0, stream, part_out, part_lse, (__bf16 *)out, lse,

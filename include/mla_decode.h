@@ -33,9 +33,10 @@
  * devices", Model-Optimizer docs, mla_attention_decode, "Parameters").
  * Chunk s of a request of length L covers tokens
  *     [s*C, min((s+1)*C, L)),
- *     C = max(32 * ceil(ceil(L / num_kv_splits) / 32), 1024);
- * trailing chunks may be empty (a request shorter than 1024 * S fills only
- * its first ceil(L / C) chunks, so no chunk is dominated by fixed costs).
+ *     C = max(32 * ceil(ceil(L / num_kv_splits) / 32), 2048);
+ * trailing chunks may be empty (a request shorter than 2048 * S fills only
+ * its first ceil(L / C) chunks, so no chunk is dominated by fixed costs and
+ * the fp32 partials stay few).
  *
  * Memory and threading contract, for every entry point:
  *   - Pointers marked "device" point to device memory allocated by the
