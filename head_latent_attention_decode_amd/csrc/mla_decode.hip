@@ -82,7 +82,7 @@ __device__ __forceinline__ T load_uniform(const T *p, long long i)
 }
 
 struct Params {
-    const __bf16 *q;            // [B, N, 576]
+    const __bf16 *q;            // [B, N, 576]  (N: every query row's heads)
     const uint8_t *cache;       // [num_blocks, P, 576] elements
     const float *cache_scale;   // fp8: one float; bf16: unused
     const int32_t *block_table; // [B, MB]
@@ -93,10 +93,12 @@ struct Params {
     float *lse;                 // [B, N] or null   (direct mode)
     float scale_log2;           // softmax_scale * log2(e)
     int B, N, S, MB, num_blocks, page_shift, HG;
-    // Query rows per request (multi-token decode): query row bq belongs to
-    // request bq / QL and is its new token bq % QL; causal rows see the
-    // request's first L - (QL - 1 - bq % QL) tokens, others all L.
-    int QL, causal;
+    // Multi-token decode: a request's QL query rows of NR heads each are its
+    // N = QL * NR heads, row-major, so that one workgroup may cover several
+    // rows.  Head h belongs to row h / NR; a causal row r sees the request's
+    // first L - (QL - 1 - r) tokens, other rows all L.  Single-token decode
+    // is QL = 1, NR = N.
+    int QL, NR, causal;
 };
 
 // XOR swizzle of the 16-byte chunks of LDS row r (rows are 1152 bytes):
@@ -125,19 +127,20 @@ __device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int
     b = bs / p.S;
 }
 
-// Token range [t0, t1) of split s of query row bq (request bq / QL).  The
-// length L is the request's, less the later new tokens a causal row may not
-// see.  The chunk length is
-// ceil(L / S) rounded up to kSplitUnit and to at least kMinChunk, a function
-// of (L, S) only.
-__device__ __forceinline__ void chunk_range(const Params &p, int bq, int s, int &t0, int &t1)
+// Request b's length, clamped to [0, the page table's capacity].
+__device__ __forceinline__ long long request_len(const Params &p, int b)
 {
     const long long cap = (long long)p.MB << p.page_shift;
-    long long L = load_uniform(p.seq_lens, bq / p.QL);
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    if (p.causal)
-        L -= p.QL - 1 - bq % p.QL;
-    L = L < 0 ? 0 : L;
+    const long long L = load_uniform(p.seq_lens, b);
+    return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Token range [t0, t1) of split s of request b.  The chunk length is
+// ceil(L / S) rounded up to kSplitUnit and to at least kMinChunk, a function
+// of (L, S) only.
+__device__ __forceinline__ void chunk_range(const Params &p, int b, int s, int &t0, int &t1)
+{
+    const long long L = request_len(p, b);
     const long long per = (L + p.S - 1) / p.S;
     long long C = (per + kSplitUnit - 1) / kSplitUnit * kSplitUnit;
     C = C > kMinChunk ? C : kMinChunk;
@@ -145,6 +148,16 @@ __device__ __forceinline__ void chunk_range(const Params &p, int bq, int s, int 
     const long long e = a + C;
     t0 = (int)(a < L ? a : L);
     t1 = (int)(e < L ? e : L);
+}
+
+// End of head h's tokens inside the chunk [t0, t1) of request b: the chunk
+// end, cut at a causal row's own length (t0 when the row has none there).
+__device__ __forceinline__ int row_end(const Params &p, int b, int h, int t0, int t1)
+{
+    if (!p.causal || p.QL == 1)
+        return t1;
+    const long long Lr = request_len(p, b) - (p.QL - 1 - h / p.NR);
+    return Lr <= t0 ? t0 : (Lr < t1 ? (int)Lr : t1);
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int num_blocks)
@@ -669,13 +682,16 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
     }
     // The row sum takes the fp32 probabilities, the MFMA their bf16
     // roundings: the LSE stays accurate to fp32 whatever the running maximum.
+    // A head that has seen no token yet (a causal row with none in this
+    // chunk) keeps m = -inf and gets zero probabilities.
+    const float mu = m == -INFINITY ? 0.f : m;
     float lsum = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         float e[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            e[j] = __builtin_amdgcn_exp2f(x[4 * tb + j] - m);
+            e[j] = __builtin_amdgcn_exp2f(x[4 * tb + j] - mu);
         lsum += (e[0] + e[1]) + (e[2] + e[3]);
         const bf16x2 p01 = to_bf16x2(e[0], e[1]);
         const bf16x2 p23 = to_bf16x2(e[2], e[3]);
@@ -745,15 +761,17 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsLds];
 
-    int bq, s, hg;
-    decode_work(p, bq, s, hg);
-    const int b = bq / p.QL;    // the request whose pages are read
-    int t_begin, t_end;
-    chunk_range(p, bq, s, t_begin, t_end);
+    int b, s, hg;
+    decode_work(p, b, s, hg);
+    int t_begin, t_chunk;
+    chunk_range(p, b, s, t_begin, t_chunk);
+    // the workgroup reads up to its last head's end (a causal row's end grows
+    // with the row index); each score wave masks at its own row's end
+    const int t_end = row_end(p, b, hg * 64 + 63, t_begin, t_chunk);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long head0 = (long long)bq * p.N + hg * 64;
+    const long long head0 = (long long)b * p.N + hg * 64;
 
     if (t_begin >= t_end) {
         // empty split: lse = -inf (its partial output is never read), or, when
@@ -806,6 +824,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
             ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
         LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * kPbufRow;
         LDS_AS float *arow = abuf + 16 * sq + r16;
+        const int t_row = row_end(p, b, hg * 64 + 16 * sq, t_begin, t_chunk);
         // fp8: the score waves take part in the tile loads (after the query
         // loads, which complete inside the page-window fill)
         WsLoader<kFp8> ld;
@@ -820,14 +839,14 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
                 ld.step(p, lds, i, ntiles);
             if (i < ntiles) {
                 const int ts = t_begin + i * kT32;
-                if (ts + kT32 <= t_end)
+                if (ts + kT32 <= t_row)
                     ws_score_tile<false>(m, l, qf, lds + (i & 3) * kStage32,
                                          prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                         g4, scale_log2, ts, t_end);
+                                         g4, scale_log2, ts, t_row);
                 else
                     ws_score_tile<true>(m, l, qf, lds + (i & 3) * kStage32,
                                         prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                        g4, scale_log2, ts, t_end);
+                                        g4, scale_log2, ts, t_row);
             }
             if (i == ntiles - 1) {
                 // final (m, l) of the wave's heads, read by the value waves
@@ -910,7 +929,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         const int hh = 32 * hb + r32;
         const float mh = mbuf[hh];
         const float lh = mbuf[64 + hh];
-        const float inv = out_scale / lh;
+        const float inv = lh > 0.f ? out_scale / lh : 0.f;   // no token: out = 0
         // lane (r32, g2) holds head hh, columns 32cb + 8q4 + 4g2 .. +4
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -1092,17 +1111,17 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveLds16];
 
-    int bq, s, hg;
-    decode_work(p, bq, s, hg);
-    const int b = bq / p.QL;    // the request whose pages are read
+    int b, s, hg;
+    decode_work(p, b, s, hg);
     int t_begin, t_end;
-    chunk_range(p, bq, s, t_begin, t_end);
+    chunk_range(p, b, s, t_begin, t_end);
+    t_end = row_end(p, b, hg * 16, t_begin, t_end);   // the 16 heads share a query row
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15;
     const int g4 = lane >> 4;
-    const long long row_b0 = (long long)bq * p.N + hg * 16;  // first head's row
+    const long long row_b0 = (long long)b * p.N + hg * 16;  // first head's row
 
     if (t_begin >= t_end) {
         // empty split: lse = -inf (its partial output is never read), or, when
@@ -1751,7 +1770,8 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     p.lse = lse;
     p.scale_log2 = softmax_scale * kLog2e;
     p.B = s->batch;
-    p.N = s->num_heads;
+    p.N = q_len * s->num_heads;     // heads of all query rows of a request
+    p.NR = s->num_heads;
     p.S = S;
     p.MB = s->max_blocks_per_seq;
     p.num_blocks = s->num_blocks;
@@ -1760,12 +1780,12 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     p.causal = causal;
     const bool direct = part_out == nullptr;
     const bool fp8 = s->cache_dtype == MLA_CACHE_FP8_E4M3FN;
-    // Kernel choice by head count and cache dtype:
-    //   N % 64 == 0:   role-split kernel, 64 heads per workgroup
-    //   otherwise:     16 heads per workgroup
-    const int heads_per_wg = s->num_heads % 64 == 0 ? 64 : 16;
-    p.HG = s->num_heads / heads_per_wg;
-    const long long grid = (long long)s->batch * q_len * S * p.HG;
+    // Kernel choice by the heads of a request (all its query rows):
+    //   a multiple of 64:  role-split kernel, 64 heads per workgroup
+    //   otherwise:         16 heads per workgroup
+    const int heads_per_wg = p.N % 64 == 0 ? 64 : 16;
+    p.HG = p.N / heads_per_wg;
+    const long long grid = (long long)s->batch * S * p.HG;
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
     const dim3 g((unsigned)grid);

@@ -232,8 +232,10 @@ mla_status_t mla_up_project(int32_t batch, int32_t num_heads, const void *latent
  * of its new token j and attends over
  *     causal != 0:  tokens [0, L - q_len + 1 + j)   (itself and what precedes)
  *     causal == 0:  tokens [0, L)
- * with the same definition, splitting and merge as mla_decode.  A row whose
- * range is empty gives out = 0, lse = -inf.
+ * with the same definition and merge as mla_decode.  The request's q_len
+ * rows share one split: the chunks of mla_decode for length L, each cut at a
+ * causal row's own end (its last chunks may be empty).  A row whose range is
+ * empty gives out = 0, lse = -inf.
  *
  *   q_len        1 .. MLA_MAX_QUERY_LEN query rows per request.
  *   q            device, bf16 [batch, q_len, num_heads, 576].
@@ -242,8 +244,9 @@ mla_status_t mla_up_project(int32_t batch, int32_t num_heads, const void *latent
  *   workspace    mla_decode_multi_workspace_size(shape, q_len, S) bytes
  *                (0 when S == 1).
  * Other arguments and errors as for mla_decode; q_len outside the range
- * gives MLA_ERR_BAD_SHAPE.  Each query row reads its request's rows through
- * the L2 of the XCD its workgroups share with the request's other rows.
+ * gives MLA_ERR_BAD_SHAPE.  The q_len * num_heads query heads of a request
+ * form the M dimension of its workgroups' contractions, so each KV tile is
+ * read once for as many of them as a workgroup holds.
  */
 size_t mla_decode_multi_workspace_size(const mla_decode_shape_t *shape, int32_t q_len,
                                        int32_t num_kv_splits);

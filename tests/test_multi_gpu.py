@@ -50,3 +50,15 @@ def test_multi_token_rejects_bad_q_len():
     with pytest.raises(mla.MLAError):
         mla.mla_decode_multi(q, d["latent_cache"], d["block_table"], d["seq_lens"],
                              wl.softmax_scale, 1)
+
+
+@pytest.mark.parametrize("QL", [4, 8])
+@pytest.mark.parametrize("S", [1, 2])
+@pytest.mark.parametrize("causal", [True, False])
+def test_multi_token_rows_share_a_workgroup(QL, S, causal):
+    """N = 16 with q_len 4 or 8: a workgroup holds 64 heads of several query
+    rows, each masked at its own causal end.  L = 2049 at S = 2 leaves a
+    one-token last chunk in which the earlier causal rows have no token, and
+    L = 2 < q_len leaves whole rows empty."""
+    wl = W.make_workload(4, 16, 64, [2, 2049, 4100, 33], seed=70 + QL + S, max_len=4160)
+    _run_and_check(wl, QL, S, causal, seed=QL * 7 + S + int(causal))
