@@ -371,12 +371,16 @@ static_assert(kWsLds <= 160 * 1024, "LDS budget");
 //     carry a tile (16 E4M3 bytes per lane), 3 for waves 0 and 1 and 2 for
 //     the others; score waves right after the barrier, value waves after
 //     their PV MFMAs.
+// NW loading waves: bf16 instructions i = v + NW m (NW = 2 or 4 divides 36),
+// fp8 loads i = v + NW m, at most kLd8<NW> per wave.
+template <int NW>
 struct WsDma {
-    static constexpr int kWaves = 4;
-    static constexpr int kDmaLo = 9;
+    static constexpr int kWaves = NW;
+    static constexpr int kDmaLo = 36 / NW;
     static constexpr int kDmaHiWaves = 0;
 };
-constexpr int kWsLd8Max = 3;       // fp8 loads per wave and tile, at most
+template <int NW>
+constexpr int kLd8 = (18 + NW - 1) / NW;
 
 // One direct-to-LDS load with a wave-uniform 64-bit base in SGPRs and a
 // 32-bit per-lane byte offset (the saddr form: no per-lane 64-bit address
@@ -395,11 +399,12 @@ __device__ __forceinline__ void dma16s(const uint8_t *sbase, int voff, LDS_AS vo
 // depend on the tile.  Instruction i fills LDS chunks [64i, 64i+64): chunk
 // q = 64i + lane is row r = q / 72, stored position q % 72, which holds
 // logical chunk (q % 72) ^ swz(r) of the row.
-__device__ __forceinline__ void ws_dma_offsets(int v, int lane, int (&off)[9])
+template <int NW>
+__device__ __forceinline__ void ws_dma_offsets(int v, int lane, int (&off)[36 / NW])
 {
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
+    for (int m = 0; m < 36 / NW; ++m) {
+        const int i = v + NW * m;
         const int q = i * 64 + lane;
         const int r = q / kRowChunks;
         const int c = (q % kRowChunks) ^ swz(r);
@@ -409,9 +414,10 @@ __device__ __forceinline__ void ws_dma_offsets(int v, int lane, int (&off)[9])
 
 // A whole bf16 tile (tile_start + 32 <= t_end): two scalar half-tile bases,
 // then value wave v's 9 loads with the precomputed offsets.
+template <int NW>
 __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
                                               LDS_AS uint8_t *stage, int v, int lane, int b,
-                                              int tile_start, const int (&off)[9])
+                                              int tile_start, const int (&off)[36 / NW])
 {
     const int pmask = (1 << p.page_shift) - 1;
     const uint8_t *base[2];
@@ -422,8 +428,8 @@ __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
         base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes;
     }
 #pragma unroll
-    for (int m = 0; m < 9; ++m) {
-        const int i = v + 4 * m;
+    for (int m = 0; m < 36 / NW; ++m) {
+        const int i = v + NW * m;
         dma16s(i < 18 ? base[0] : base[1], off[m], stage + i * 1024);
     }
 }
@@ -433,21 +439,23 @@ __device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
 // 2c+1 of the row, stored at positions (2c) ^ swz(r) and that ^ 1.  Source
 // offsets are relative to the first row of the load's half-tile (i / 9);
 // destination offsets are relative to the stage.  Every wave issues
-// kWsLd8Max loads, so that no register is loaded on one path only (the
+// kLd8<NW> loads, so that no register is loaded on one path only (the
 // compiler would then copy it, and wait for the load, at the loop's end): a
 // wave whose third load index passes 17 repeats its first load and does not
 // write it.
+template <int NW>
 __device__ __forceinline__ int ws_ld8_index(int w, int m)
 {
-    const int i = w + 8 * m;
+    const int i = w + NW * m;
     return i < 18 ? i : w;
 }
-__device__ __forceinline__ void ws_ld8_offsets(int w, int lane, int (&src)[kWsLd8Max],
-                                               int (&dst)[kWsLd8Max])
+template <int NW>
+__device__ __forceinline__ void ws_ld8_offsets(int w, int lane, int (&src)[kLd8<NW>],
+                                               int (&dst)[kLd8<NW>])
 {
 #pragma unroll
-    for (int m = 0; m < kWsLd8Max; ++m) {
-        const int i = ws_ld8_index(w, m);
+    for (int m = 0; m < kLd8<NW>; ++m) {
+        const int i = ws_ld8_index<NW>(w, m);
         const int q = i * 64 + lane;
         const int r = q / 36, c = q % 36;
         src[m] = (r - 16 * (i / 9)) * kRowBytes8 + c * 16;
@@ -464,9 +472,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t *base)
 }
 
 // The wave's loads of a whole fp8 tile into registers.
+template <int NW>
 __device__ __forceinline__ void ws_ld8_full(const Params &p, PageWindow &win, int w, int lane,
-                                            int b, int tile_start, const int (&src)[kWsLd8Max],
-                                            u32x4 (&r)[kWsLd8Max])
+                                            int b, int tile_start, const int (&src)[kLd8<NW>],
+                                            u32x4 (&r)[kLd8<NW>])
 {
     const int pmask = (1 << p.page_shift) - 1;
     __amdgpu_buffer_rsrc_t rs[2];
@@ -478,17 +487,18 @@ __device__ __forceinline__ void ws_ld8_full(const Params &p, PageWindow &win, in
                           (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes8);
     }
 #pragma unroll
-    for (int m = 0; m < kWsLd8Max; ++m) {
-        const int i = ws_ld8_index(w, m);
+    for (int m = 0; m < kLd8<NW>; ++m) {
+        const int i = ws_ld8_index<NW>(w, m);
         r[m] = __builtin_amdgcn_raw_buffer_load_b128(i < 9 ? rs[0] : rs[1], src[m], 0, 0);
     }
 }
 
 // The last, partial fp8 tile: rows past t_end repeat row t_end - 1 (finite
 // values whose scores are masked), so every LDS row holds a real row.
+template <int NW>
 __device__ __forceinline__ void ws_ld8_part(const Params &p, PageWindow &win, int w, int lane,
                                             int b, int tile_start, int t_end,
-                                            u32x4 (&r)[kWsLd8Max])
+                                            u32x4 (&r)[kLd8<NW>])
 {
     const int last = t_end - 1;
     const int pmask = (1 << p.page_shift) - 1;
@@ -501,8 +511,8 @@ __device__ __forceinline__ void ws_ld8_part(const Params &p, PageWindow &win, in
         rs[h] = rows_rsrc(p.cache + ((long long)blk << p.page_shift) * kRowBytes8);
     }
 #pragma unroll
-    for (int m = 0; m < kWsLd8Max; ++m) {
-        const int i = ws_ld8_index(w, m);
+    for (int m = 0; m < kLd8<NW>; ++m) {
+        const int i = ws_ld8_index<NW>(w, m);
         const int q = i * 64 + lane;
         const int rr = q / 36;
         int tok = tile_start + rr;
@@ -514,12 +524,13 @@ __device__ __forceinline__ void ws_ld8_part(const Params &p, PageWindow &win, in
 
 // Widen the wave's loads of a tile to bf16 and write them at their swizzled
 // positions of the stage: two 16-byte writes per load.
-__device__ __forceinline__ void ws_st8(LDS_AS uint8_t *stage, int w, const int (&dst)[kWsLd8Max],
-                                       const u32x4 (&r)[kWsLd8Max])
+template <int NW>
+__device__ __forceinline__ void ws_st8(LDS_AS uint8_t *stage, int w, const int (&dst)[kLd8<NW>],
+                                       const u32x4 (&r)[kLd8<NW>])
 {
 #pragma unroll
-    for (int m = 0; m < kWsLd8Max; ++m) {
-        if (w + 8 * m < 18) {
+    for (int m = 0; m < kLd8<NW>; ++m) {
+        if (w + NW * m < 18) {
             const u32x2 a = e4m3x4_to_bf16x4(r[m][0]);
             const u32x2 b = e4m3x4_to_bf16x4(r[m][1]);
             const u32x2 c = e4m3x4_to_bf16x4(r[m][2]);
@@ -532,14 +543,13 @@ __device__ __forceinline__ void ws_st8(LDS_AS uint8_t *stage, int w, const int (
 
 // All of a wave's tile traffic: its share of the loads of each tile and,
 // for an fp8 cache, the registers that carry them to the stage.  w is the
-// wave's index among the loading waves (value waves 0..3 for bf16, all
-// waves 0..7 for fp8).
-template <bool kFp8>
+// wave's index among the NW loading waves.
+template <bool kFp8, int NW>
 struct WsLoader {
     PageWindow win;
-    int off[kFp8 ? kWsLd8Max : 9];
-    int dst[kFp8 ? kWsLd8Max : 1];
-    u32x4 rg[kFp8 ? kWsLd8Max : 1];
+    int off[kFp8 ? kLd8<NW> : 36 / NW];
+    int dst[kFp8 ? kLd8<NW> : 1];
+    u32x4 rg[kFp8 ? kLd8<NW> : 1];
     int w, lane, b, t_begin, t_end;
 
     __device__ __forceinline__ void init(const Params &p, int w_, int lane_, int b_, int t0,
@@ -551,9 +561,9 @@ struct WsLoader {
         t_begin = t0;
         t_end = t1;
         if constexpr (kFp8)
-            ws_ld8_offsets(w, lane, off, dst);
+            ws_ld8_offsets<NW>(w, lane, off, dst);
         else
-            ws_dma_offsets(w, lane, off);
+            ws_dma_offsets<NW>(w, lane, off);
         window_fill(p, win, b, t_begin >> p.page_shift, lane);
     }
     // bf16: direct-to-LDS loads of tile t into its stage
@@ -562,25 +572,25 @@ struct WsLoader {
         const int ts = t_begin + t * kT32;
         LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
         if (ts + kT32 <= t_end)
-            ws_issue_full(p, win, stage, w, lane, b, ts, off);
+            ws_issue_full<NW>(p, win, stage, w, lane, b, ts, off);
         else
-            issue_tile_dma<WsDma>(p, win, stage, w, lane, b, ts, t_end);
+            issue_tile_dma<WsDma<NW>>(p, win, stage, w, lane, b, ts, t_end);
     }
     // bf16: wait until at most k of this wave's tiles are in flight
-    __device__ __forceinline__ void wait(int k) { wait_tiles_dma<WsDma>(w, k); }
+    __device__ __forceinline__ void wait(int k) { wait_tiles_dma<WsDma<NW>>(w, k); }
     // fp8: loads of tile t into the registers
     __device__ __forceinline__ void load(const Params &p, int t)
     {
         const int ts = t_begin + t * kT32;
         if (ts + kT32 <= t_end)
-            ws_ld8_full(p, win, w, lane, b, ts, off, rg);
+            ws_ld8_full<NW>(p, win, w, lane, b, ts, off, rg);
         else
-            ws_ld8_part(p, win, w, lane, b, ts, t_end, rg);
+            ws_ld8_part<NW>(p, win, w, lane, b, ts, t_end, rg);
     }
     // fp8: the registers, widened, into tile t's stage
     __device__ __forceinline__ void store(LDS_AS uint8_t *lds, int t)
     {
-        ws_st8(lds + (t & 3) * kStage32, w, dst, rg);
+        ws_st8<NW>(lds + (t & 3) * kStage32, w, dst, rg);
     }
     // Before the first barrier: tiles 0 and 1 issued (bf16), or written with
     // tile 2 in the registers (fp8).
@@ -756,6 +766,90 @@ __device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], bf16x8 (&vt)[8]
     }
 }
 
+// Transposed-read offsets of value wave vq (columns 128vq .. +128): 16-lane
+// group G reads token rows 16kk + 8 g2 + 4h + (j >> 2) of columns
+// 128vq + 32cb + 16(G & 1) + 4(j & 3) (the A operand of O^T = V^T . P^T).
+__device__ __forceinline__ void ws_value_offsets(int vq, int lane, int (&to)[2][2])
+{
+    const int g2 = lane >> 5, G = lane >> 4, j = lane & 15;
+    const int cl = 2 * (G & 1) + ((j >> 1) & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rr = 4 * h + (j >> 2);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            to[h][e] = (8 * g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 + 8 * (j & 1) +
+                       256 * vq;
+    }
+}
+
+// Value-wave epilogue of the role-split kernels: normalise O and write the
+// output (direct) or the fp32 partial and lse of each of the 64 heads.
+template <bool kDirect>
+__device__ __forceinline__ void ws_value_epilogue(const Params &p, const f32x16 (&o)[4][2],
+                                                  LDS_AS uint8_t *xr, const LDS_AS float *mbuf,
+                                                  long long head0, int s, int vq, int lane,
+                                                  float out_scale)
+{
+    constexpr int kXRow = 528;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    // The accumulator layout scatters a store instruction over 32 head rows,
+    // so the normalised output goes through a wave-private LDS region xr
+    // (32 rows of 528 bytes) first, one head block (32 heads x 128 columns)
+    // at a time, and leaves as whole row segments: 128 columns of one head,
+    // 512 contiguous bytes (fp32 partial) or 256 (bf16 output).  Rows are
+    // padded to 528 bytes so the column-block writes spread over the banks.
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const int hh = 32 * hb + r32;
+        const float mh = mbuf[hh];
+        const float lh = mbuf[64 + hh];
+        const float inv = lh > 0.f ? out_scale / lh : 0.f;   // no token: out = 0
+        // lane (r32, g2) holds head hh, columns 32cb + 8q4 + 4g2 .. +4
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16 &a = o[cb][hb];
+                *(LDS_AS f32x4 *)(xr + r32 * kXRow + (cb * 32 + q4 * 8 + g2 * 4) * 4) =
+                    f32x4{a[4 * q4] * inv, a[4 * q4 + 1] * inv, a[4 * q4 + 2] * inv,
+                          a[4 * q4 + 3] * inv};
+            }
+        const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the region is written
+        if (kDirect) {
+            // 4 heads per instruction: lane l reads head 4it + (l >> 4),
+            // columns 8 (l & 15) .. +8
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int h = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+                const f32x4 v0 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
+                const f32x4 v1 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4 + 16);
+                const bf16x2 a0 = to_bf16x2(v0[0], v0[1]), a1 = to_bf16x2(v0[2], v0[3]);
+                const bf16x2 a2 = to_bf16x2(v1[0], v1[1]), a3 = to_bf16x2(v1[2], v1[3]);
+                *(bf16x8 *)(p.out + (head0 + 32 * hb + h) * kDV + 128 * vq + c) =
+                    bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+            }
+            if (p.lse && vq == 0 && g2 == 0)
+                p.lse[head0 + hh] = lse_nat;
+        } else {
+            // 2 heads per instruction: lane l reads head 2it + (l >> 5),
+            // columns 4 (l & 31) .. +4
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int h = 2 * it + (lane >> 5), c = 4 * (lane & 31);
+                *(f32x4 *)(p.part_out + ((head0 + 32 * hb + h) * p.S + s) * kDV + 128 * vq + c) =
+                    *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
+            }
+            if (vq == 0 && g2 == 0)
+                p.part_lse[(head0 + hh) * p.S + s] = lse_nat;
+        }
+        // the reads of this head block are done before the next one
+        // overwrites the region
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+}
+
 template <bool kDirect, bool kFp8>
 __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 {
@@ -827,7 +921,7 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         const int t_row = row_end(p, b, hg * 64 + 16 * sq, t_begin, t_chunk);
         // fp8: the score waves take part in the tile loads (after the query
         // loads, which complete inside the page-window fill)
-        WsLoader<kFp8> ld;
+        WsLoader<kFp8, kFp8 ? 8 : 4> ld;
         if constexpr (kFp8) {
             ld.init(p, w, lane, b, t_begin, t_end);
             ld.prologue(p, lds, ntiles);
@@ -870,19 +964,8 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     const int r32 = lane & 31, g2 = lane >> 5;
     const int vq = w - 4;
     int to[2][2];
-    {
-        const int G = lane >> 4, j = lane & 15;
-        const int cl = 2 * (G & 1) + ((j >> 1) & 1);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int rr = 4 * h + (j >> 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                to[h][e] = (8 * g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 +
-                           8 * (j & 1) + 256 * vq;
-        }
-    }
-    WsLoader<kFp8> ld;
+    ws_value_offsets(vq, lane, to);
+    WsLoader<kFp8, kFp8 ? 8 : 4> ld;
     ld.init(p, kFp8 ? w : vq, lane, b, t_begin, t_end);
     ld.prologue(p, lds, ntiles);
     f32x16 o[4][2];
@@ -913,66 +996,11 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
             ld.step(p, lds, i, ntiles);
     }
 
-    // ---- value-wave epilogue.  The accumulator layout scatters a store
-    // instruction over 32 head rows, so the normalised output goes through a
-    // wave-private LDS region first, one head block (32 heads x 128 columns)
-    // at a time, and leaves as whole row segments: 128 columns of one head,
-    // 512 contiguous bytes (fp32 partial) or 256 (bf16 output).  After the
-    // last barrier the value waves read only stage (ntiles-1)%4 and no load
-    // is in flight, so stages ntiles%4 and (ntiles+1)%4 are free: waves 0, 1
-    // take the first, waves 2, 3 the second.  Rows are padded to 528 bytes so
-    // the column-block writes spread over the banks.
-    constexpr int kXRow = 528;
-    LDS_AS uint8_t *xr = stage_of_ws(lds, ntiles + (vq >> 1)) + (vq & 1) * 32 * kXRow;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const int hh = 32 * hb + r32;
-        const float mh = mbuf[hh];
-        const float lh = mbuf[64 + hh];
-        const float inv = lh > 0.f ? out_scale / lh : 0.f;   // no token: out = 0
-        // lane (r32, g2) holds head hh, columns 32cb + 8q4 + 4g2 .. +4
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x16 &a = o[cb][hb];
-                *(LDS_AS f32x4 *)(xr + r32 * kXRow + (cb * 32 + q4 * 8 + g2 * 4) * 4) =
-                    f32x4{a[4 * q4] * inv, a[4 * q4 + 1] * inv, a[4 * q4 + 2] * inv,
-                          a[4 * q4 + 3] * inv};
-            }
-        const float lse_nat = (mh + __builtin_amdgcn_logf(lh)) * kLn2;
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the region is written
-        if (kDirect) {
-            // 4 heads per instruction: lane l reads head 4it + (l >> 4),
-            // columns 8 (l & 15) .. +8
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int h = 4 * it + (lane >> 4), c = 8 * (lane & 15);
-                const f32x4 v0 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
-                const f32x4 v1 = *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4 + 16);
-                const bf16x2 a0 = to_bf16x2(v0[0], v0[1]), a1 = to_bf16x2(v0[2], v0[3]);
-                const bf16x2 a2 = to_bf16x2(v1[0], v1[1]), a3 = to_bf16x2(v1[2], v1[3]);
-                *(bf16x8 *)(p.out + (head0 + 32 * hb + h) * kDV + 128 * vq + c) =
-                    bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-            }
-            if (p.lse && vq == 0 && g2 == 0)
-                p.lse[head0 + hh] = lse_nat;
-        } else {
-            // 2 heads per instruction: lane l reads head 2it + (l >> 5),
-            // columns 4 (l & 31) .. +4
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int h = 2 * it + (lane >> 5), c = 4 * (lane & 31);
-                *(f32x4 *)(p.part_out + ((head0 + 32 * hb + h) * p.S + s) * kDV + 128 * vq + c) =
-                    *(const LDS_AS f32x4 *)(xr + h * kXRow + c * 4);
-            }
-            if (vq == 0 && g2 == 0)
-                p.part_lse[(head0 + hh) * p.S + s] = lse_nat;
-        }
-        // the reads of this head block are done before the next one
-        // overwrites the region
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-    }
+    // After the last barrier the value waves read only stage (ntiles-1)%4
+    // and no load is in flight, so stages ntiles%4 and (ntiles+1)%4 are free:
+    // value waves 0, 1 take the first, 2, 3 the second.
+    ws_value_epilogue<kDirect>(p, o, stage_of_ws(lds, ntiles + (vq >> 1)) + (vq & 1) * 32 * 528,
+                               mbuf, head0, s, vq, lane, out_scale);
 }
 
 // ===========================================================================
