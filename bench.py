@@ -316,7 +316,6 @@ def run_insert(args):
     T, N, P = spec["B"], spec["N"], spec["page_size"]
     nb = max(T, 4096 // P) * 4
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
     copies = []
     for c in range(max(1, args.copies)):
         x = W.make_insert_inputs(T, N, nb, P, seed=4242 + c, cache_dtype=cache_dtype)
@@ -330,23 +329,9 @@ def run_insert(args):
             d["cache_dtype"] = cache_dtype
         copies.append((x, d))
 
-    def call(d):
-        mla.concat_q_insert_cache(**d)
-
-    for i in range(args.warmup):
-        call(copies[i % len(copies)][1])
-    torch.cuda.synchronize()
+    calls = [(lambda d=d: mla.concat_q_insert_cache(**d)) for _, d in copies]
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        call(copies[i % len(copies)][1])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kernel_ms, wall = _time_graph(calls, args.warmup, K)
     esz = 1 if cache_dtype == "fp8_e4m3fn" else 2
     nbytes = T * N * W.HEAD_SIZE * 2 * 2 + T * W.HEAD_SIZE * (2 + esz) + T * 8 + \
         (4 if esz == 1 else 0)
@@ -410,6 +395,37 @@ def _time_calls(calls, warmup, steps):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
+
+
+def _time_graph(calls, warmup, steps):
+    """For kernels shorter than a host launch: warm up, capture `steps` calls
+    (rotating over `calls`) in one HIP graph, replay it once untimed, then time
+    one replay with HIP events on the replay stream.  Returns (ms per launch,
+    wall s of the timed replay): back-to-back launches with no host gaps, so
+    the average is the kernel's own duration plus the graph's launch spacing."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                calls[i % len(calls)]()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
 
 
 def _op_line(metric, nbytes, kernel_ms, wall, steps, warmup, kernel, workload, dtype, cpu,
@@ -586,7 +602,7 @@ def run_projection(args):
         copies.append((d, out))
     fn = mla.absorb_query if absorb else mla.up_project
     calls = [(lambda d=d, o=o: fn(d[0], d[1], out=o)) for d, o in copies]
-    kernel_ms, wall = _time_calls(calls, args.warmup, args.steps)
+    kernel_ms, wall = _time_graph(calls, args.warmup, args.steps)
     nbytes = N * K * M * 2 + B * N * (K + M) * 2
     flops = 2 * B * N * K * M
     name = "absorb (q_nope . W_UK_T)" if absorb else "up-projection (latent . W_UV)"

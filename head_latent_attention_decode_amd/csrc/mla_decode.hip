@@ -1668,80 +1668,108 @@ __global__ __launch_bounds__(256) void mla_merge_two(
 // ===========================================================================
 // Per-head matmuls around the attention: out[b, n, c] = sum_k x[b, n, k] *
 // W[n, k, c], the query absorb (K = 128, M = 512, W = W_UK_T) and the output
-// up-projection (K = 512, M = 128, W = W_UV).  One single-wave workgroup per
-// (head, 32-column block), so that several overlap on a CU while each stages
-// its block of W (K rows x 32 columns, rows padded to 80 bytes) in LDS.  The
-// block is read transposed with ds_read_b64_tr_b16 as the A operand of
-// v_mfma_f32_32x32x16_bf16 computing out^T = W^T . x^T, so a lane's results
-// are 4 consecutive columns of one row; the batch is walked 32 rows at a
-// time, each block's x slice (16 bytes per lane and k step) loaded into
-// registers at once.
+// up-projection (K = 512, M = 128, W = W_UV).  Both are bound by HBM (a
+// weight is used by only B tokens), so a workgroup issues every load it needs
+// at once and keeps no loop: 4 waves on one unit (head n, a block of kMb
+// columns, a block of 64 batch rows).  The W block (K rows x kMb
+// columns) is staged in LDS, rows padded by 16 bytes, and read transposed
+// with ds_read_b64_tr_b16 as the A operand of v_mfma_f32_16x16x32_bf16
+// computing out^T = W^T . x^T; wave w takes rows 16w .. 16w+15, its x
+// fragments (16 bytes per lane and 32-deep k step) loaded straight into
+// registers.  The results go back through LDS (over the W block, after a
+// barrier) so that every store instruction writes whole output rows.
+// Units are numbered head-major and dealt out so that the units of one head
+// run back to back on one XCD (workgroup i runs on XCD i mod 8): the W block
+// of each row block and the x rows of each column block are re-read from that
+// XCD's L2, not from HBM.
 // ===========================================================================
-template <int K>
-__global__ __launch_bounds__(64) void mla_head_mm(const __bf16 *__restrict__ x, long long xs_tok,
-                                                  long long xs_head, const __bf16 *__restrict__ w,
-                                                  __bf16 *__restrict__ out, int B, int N, int M)
+template <int K, int kMb>
+__global__ __launch_bounds__(256) void mla_head_mm(const __bf16 *__restrict__ x, long long xs_tok,
+                                                   long long xs_head, const __bf16 *__restrict__ w,
+                                                   __bf16 *__restrict__ out, int B, int N, int M)
 {
-    constexpr int kRow = 80;
+    constexpr int kRow = kMb * 2 + 16;          // padded LDS row (W block and results)
+    constexpr int kSteps = K / 32;              // k steps of one MFMA
+    constexpr int kCt = kMb / 16;               // 16-column output tiles
+    constexpr int kChunks = kMb / 8;            // 16-byte chunks per W or output row
+    constexpr int kRowsPerLd = 256 / kChunks;   // W rows one load instruction covers
+    constexpr int kWLd = K / kRowsPerLd;        // W loads per thread
+    constexpr int kRowsPerSt = 64 / kChunks;    // output rows one store instruction covers
+    static_assert(K % kRowsPerLd == 0 && kMb % 16 == 0 && 64 % kChunks == 0, "tiling");
+    static_assert(64 <= K && 16 % kRowsPerSt == 0, "the result tiles fit over the W block");
     __shared__ __attribute__((aligned(16))) uint8_t smem[K * kRow];
     LDS_AS uint8_t *lds = AS3(smem);
-    const int nblk = M / 32;
-    const int n = blockIdx.x / nblk, c0 = (blockIdx.x % nblk) * 32;
-    const int lane = threadIdx.x;
-    const __bf16 *wn = w + (long long)n * K * M + c0;
-    const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
-    // the x fragments of one 32-row block, all K / 16 of them in registers;
-    // the first block's loads are in flight while W is staged
-    constexpr int kSteps = K / 16;
-    bf16x8 xf[kSteps];
-    auto load_x = [&](int rb) {
-        const int row = rb + r32;
-        const bool live = row < B;
-        const __bf16 *xr = x + (long long)(live ? row : 0) * xs_tok + (long long)n * xs_head + 8 * g2;
+    const int nblk = M / kMb, nrb = (B + 63) / 64;
+    const unsigned U = (unsigned)N * (unsigned)nblk * (unsigned)nrb;
+    const unsigned i = blockIdx.x;
+    const unsigned u = (U & 7) ? i : (i & 7) * (U >> 3) + (i >> 3);
+    const int rb = (int)(u % (unsigned)nrb);
+    const int cb = (int)((u / (unsigned)nrb) % (unsigned)nblk);
+    const int n = (int)(u / (unsigned)nrb / (unsigned)nblk);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, kq = lane >> 4;
+    const int wrow0 = rb * 64 + wave * 16;      // first batch row of this wave
+    // W block: thread t loads chunk t % kChunks of rows t / kChunks + kRowsPerLd * m
+    const int wrow = tid / kChunks, wchunk = tid % kChunks;
+    const __bf16 *wn = w + (long long)n * K * M + (long long)cb * kMb + 8 * wchunk;
+    bf16x8 wv[kWLd];
 #pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks)
-            xf[ks] = live ? *(const bf16x8 *)(xr + 16 * ks) : bf16x8{};
-    };
-    load_x(0);
-    // 4 chunks of 16 bytes per row: lane l stages chunk l & 3 of rows l >> 2, +16, ...
-#pragma unroll 8
-    for (int r = lane >> 2; r < K; r += 16)
-        *(LDS_AS bf16x8 *)(lds + r * kRow + (lane & 3) * 16) =
-            *(const bf16x8 *)(wn + (long long)r * M + 8 * (lane & 3));
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    // group G loads rows 8(G >> 1) + 4h + (j >> 2) (+16 ks), columns
-    // 16(G & 1) + 4(j & 3) .. +4; lane j then holds column j of the group's 16
-    // (W^T row r32) at 4 consecutive rows (k)
+    for (int m = 0; m < kWLd; ++m)
+        wv[m] = *(const bf16x8 *)(wn + (long long)(wrow + kRowsPerLd * m) * M);
+    // x fragments of this wave's rows (rows past the batch read the last row
+    // and are not stored)
+    bf16x8 xf[kSteps];
+    const __bf16 *xr = x + (long long)min(wrow0 + j, B - 1) * xs_tok + (long long)n * xs_head + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks)
+        xf[ks] = *(const bf16x8 *)(xr + 32 * ks);
+#pragma unroll
+    for (int m = 0; m < kWLd; ++m)
+        *(LDS_AS bf16x8 *)(lds + (wrow + kRowsPerLd * m) * kRow + 16 * wchunk) = wv[m];
+    __syncthreads();
+    // (a wave whose rows all lie past the batch computes on the clamped row
+    // and stores nothing: an early exit here would let the compiler sink the
+    // x loads below the barrier, after the W block has arrived)
+    // lane j of group kq reads rows 8kq + 4h + (j >> 2), columns 4(j & 3) .. +4
+    // of a 16-column tile and then holds column j at 4 consecutive rows
     int toff[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        toff[h] = (8 * (G >> 1) + 4 * h + (j >> 2)) * kRow + (16 * (G & 1) + 4 * (j & 3)) * 2;
-    for (int rb = 0; rb < B; rb += 32) {
-        const int row = rb + r32;
-        const bool live = row < B;
-        if (rb > 0)
-            load_x(rb);
-        f32x16 acc = f32x16{};
+        toff[h] = (8 * kq + 4 * h + (j >> 2)) * kRow + 8 * (j & 3);
+    f32x4 acc[kCt];
 #pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks) {
+    for (int ct = 0; ct < kCt; ++ct)
+        acc[ct] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4 *)(lds + toff[0] + ks * 16 * kRow));
+                (LDS_AS bf16x4 *)(lds + toff[0] + ks * 32 * kRow + ct * 32));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4 *)(lds + toff[1] + ks * 16 * kRow));
+                (LDS_AS bf16x4 *)(lds + toff[1] + ks * 32 * kRow + ct * 32));
             const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[ks], acc, 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf[ks], acc[ct], 0, 0, 0);
         }
-        // lane (r32, g2): batch row r32, columns 8q + 4g2 .. +4 of the block
-        if (live) {
-            __bf16 *o = out + ((long long)row * N + n) * M + c0 + 4 * g2;
+    }
+    // lane (j, kq) holds row j, columns 16ct + 4kq .. +4: write the wave's
+    // rows into its own slice of the (now unused) W block, then store whole rows
+    __syncthreads();
+    LDS_AS uint8_t *tile = lds + wave * 16 * kRow;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bf16x2 p01 = to_bf16x2(acc[4 * q], acc[4 * q + 1]);
-                const bf16x2 p23 = to_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
-                *(bf16x4 *)(o + 8 * q) = bf16x4{p01[0], p01[1], p23[0], p23[1]};
-            }
-        }
+    for (int ct = 0; ct < kCt; ++ct) {
+        const bf16x2 p01 = to_bf16x2(acc[ct][0], acc[ct][1]);
+        const bf16x2 p23 = to_bf16x2(acc[ct][2], acc[ct][3]);
+        *(LDS_AS bf16x4 *)(tile + j * kRow + (16 * ct + 4 * kq) * 2) =
+            bf16x4{p01[0], p01[1], p23[0], p23[1]};
+    }
+    const int sr = lane / kChunks, sc = lane % kChunks;
+#pragma unroll
+    for (int s = 0; s < 16 / kRowsPerSt; ++s) {
+        const int r = s * kRowsPerSt + sr;
+        const bf16x8 v = *(const LDS_AS bf16x8 *)(tile + r * kRow + 16 * sc);
+        if (wrow0 + r < B)
+            *(bf16x8 *)(out + ((long long)(wrow0 + r) * N + n) * M + (long long)cb * kMb + 8 * sc) = v;
     }
 }
 
@@ -2030,19 +2058,22 @@ static mla_status_t launch_head_mm(int K, int M, int32_t batch, int32_t num_head
         return MLA_ERR_NULL_POINTER;
     // 16-byte loads of x and of W rows
     if ((x_token_stride | x_head_stride) & 7 || ((uintptr_t)x & 15) || ((uintptr_t)w & 15) ||
-        ((uintptr_t)out & 7))
+        ((uintptr_t)out & 15))
         return MLA_ERR_UNSUPPORTED;
-    const long long grid = (long long)num_heads * (M / 32);
+    // units of (head, column block, 64-row block): the absorb takes 128-column
+    // blocks (32 KB of W each), the up-projection 64-column blocks (64 KB)
+    const int mb = K == 128 ? 128 : 64;
+    const long long grid = (long long)num_heads * (M / mb) * ((batch + 63) / 64);
     if (grid > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
+    const dim3 g((unsigned)grid), blk(256);
+    const __bf16 *xb = (const __bf16 *)x, *wb = (const __bf16 *)w;
+    __bf16 *ob = (__bf16 *)out;
+    const long long ts = x_token_stride, hs = x_head_stride;
     if (K == 128)
-        hipLaunchKernelGGL(mla_head_mm<128>, dim3((unsigned)grid), dim3(64), 0, stream,
-                           (const __bf16 *)x, (long long)x_token_stride, (long long)x_head_stride,
-                           (const __bf16 *)w, (__bf16 *)out, batch, num_heads, M);
+        hipLaunchKernelGGL((mla_head_mm<128, 128>), g, blk, 0, stream, xb, ts, hs, wb, ob, batch, num_heads, M);
     else
-        hipLaunchKernelGGL(mla_head_mm<512>, dim3((unsigned)grid), dim3(64), 0, stream,
-                           (const __bf16 *)x, (long long)x_token_stride, (long long)x_head_stride,
-                           (const __bf16 *)w, (__bf16 *)out, batch, num_heads, M);
+        hipLaunchKernelGGL((mla_head_mm<512, 64>), g, blk, 0, stream, xb, ts, hs, wb, ob, batch, num_heads, M);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

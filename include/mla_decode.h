@@ -211,7 +211,7 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
  *   w_uv        device, bf16 [N, 512, 128], contiguous.
  *   out         device, bf16 [batch, N, 128], contiguous.
  * Strides are in elements and must be multiples of 8, the input and weight
- * pointers 16-byte aligned and the output 8-byte aligned, else
+ * pointers and the output 16-byte aligned, else
  * MLA_ERR_UNSUPPORTED.  Negative sizes or strides: MLA_ERR_BAD_SHAPE.
  * Missing pointers: MLA_ERR_NULL_POINTER.
  */

@@ -21,7 +21,7 @@ def _rel_rows(got, ref):
     return (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max()
 
 
-@pytest.mark.parametrize("B,N", [(1, 16), (37, 16), (64, 128), (256, 128), (5, 8)])
+@pytest.mark.parametrize("B,N", [(1, 16), (37, 16), (64, 128), (256, 128), (5, 8), (100, 24), (3, 3), (300, 16)])
 def test_absorb_and_up_project_match_oracle(B, N):
     x = W.make_projection_inputs(B, N, seed=B * 3 + N)
     w_uk_t = x.W_UK.permute(1, 2, 0).contiguous().to(DEV)
