@@ -239,18 +239,24 @@ def main():
           for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    last = torch.cuda.Event(enable_timing=True)
     for i in range(K):
         st = copies[i % len(copies)]
         ev[i][0].record(stream)
         st.split()
         ev[i][1].record(stream)
         st.merge()
+    last.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / K
     # event time of the split kernel alone, on its stream, every timed step
-    split_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    split_each = np.array([a.elapsed_time(b) for a, b in ev])
+    split_ms = float(split_each.mean())
+    # each step on the GPU's own clock: from one split's start to the next
+    step_each = np.array([ev[i][0].elapsed_time(ev[i + 1][0]) for i in range(K - 1)] +
+                         [ev[K - 1][0].elapsed_time(last)])
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -271,6 +277,8 @@ def main():
     roof["traffic"] = measured_traffic(wl)
     roof["kernel"] = split_kernel_name(wl)
     roof["kernel_ms"] = round(split_ms, 5)
+    roof["kernel_us_p10_p50_p90"] = [round(float(v) * 1e3, 2)
+                                     for v in np.percentile(split_each, [10, 50, 90])]
 
     cpu = cpu_baseline(wl, args.cpu_requests) if args.cpu_requests > 0 else None
     lens = wl.seq_lens
@@ -283,6 +291,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_us_p10_p50_p90": [round(float(v) * 1e3, 2)
+                                for v in np.percentile(step_each, [10, 50, 90])],
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "decode_tokens_per_s": round(wl.B / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(int(lens.sum()) / (ms_per_step * 1e-3), 1),

@@ -1341,31 +1341,65 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 //   slots x 8 column groups of 8, and the slots' sums are added through LDS.
 // ===========================================================================
 // Largest state lse of a row and the row's total lse (natural log).
-__device__ __forceinline__ void merge_total(const float *ls, int S, float &M, float &total)
+__device__ __forceinline__ void merge_total(const float *ls, int S, int lane, float &M,
+                                            float &total)
 {
     M = -INFINITY;
-    for (int s = 0; s < S; ++s)
+    for (int s = lane; s < S; s += 64)
         M = fmaxf(M, ls[s]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        M = fmaxf(M, __shfl_xor(M, d));
     float Z = 0.f;
-    for (int s = 0; s < S; ++s)
-        Z += __builtin_amdgcn_exp2f((ls[s] - M) * kLog2e);
+    if (M != -INFINITY)
+        for (int s = lane; s < S; s += 64)
+            Z += __builtin_amdgcn_exp2f((ls[s] - M) * kLog2e);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        Z += __shfl_xor(Z, d);
     total = M + __builtin_amdgcn_logf(Z) * kLn2;
 }
 
-// Weighted sum of the live states s0, s0 + step, ... of one row over this
-// lane's 8 columns.
-__device__ __forceinline__ void merge_sum(const float *po, const float *ls, int S, int s0,
-                                          int step, float total, f32x4 &acc0, f32x4 &acc1)
+// Weighted sum of a row's live states over this lane's 8 columns.  The live
+// states of each group of 64 are found with one ballot and taken 4 at a time,
+// so that a round's loads are all in flight before the first is used; a round
+// with fewer than 4 left repeats its last state at weight zero (a live state's
+// values are finite).  States of weight zero are never loaded.
+__device__ __forceinline__ void merge_sum(const float *po, const float *ls, int S, int lane,
+                                          float total, f32x4 &acc0, f32x4 &acc1)
 {
-    for (int s = s0; s < S; s += step) {
-        const float l = ls[s];
-        if (l == -INFINITY)
-            continue;
-        const float wgt = __builtin_amdgcn_exp2f((l - total) * kLog2e);
-        const f32x4 v0 = *(const f32x4 *)(po + (long long)s * kDV);
-        const f32x4 v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
-        acc0 += wgt * v0;
-        acc1 += wgt * v1;
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        const float lv = c0 + lane < S ? ls[c0 + lane] : -INFINITY;
+        unsigned long long live = __ballot(lv != -INFINITY);
+        while (live) {
+            int idx[4];
+            float wgt[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (live) {
+                    idx[u] = __builtin_ctzll(live);
+                    live &= live - 1;
+                    const float l = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), idx[u]));
+                    wgt[u] = __builtin_amdgcn_exp2f((l - total) * kLog2e);
+                } else {
+                    idx[u] = idx[u > 0 ? u - 1 : 0];
+                    wgt[u] = 0.f;
+                }
+            }
+            f32x4 v[4][2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float *src = po + (long long)(c0 + idx[u]) * kDV;
+                v[u][0] = *(const f32x4 *)src;
+                v[u][1] = *(const f32x4 *)(src + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc0 += wgt[u] * v[u][0];
+                acc1 += wgt[u] * v[u][1];
+            }
+        }
     }
 }
 
@@ -1391,7 +1425,7 @@ __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_
     const int lane = threadIdx.x & 63;
     const float *ls = part_lse + (long long)row * S;
     float M, total;
-    merge_total(ls, S, M, total);
+    merge_total(ls, S, lane, M, total);
     __bf16 *o = out + (long long)row * kDV + lane * 8;
     if (M == -INFINITY) {
         *(bf16x8 *)o = bf16x8{};
@@ -1400,7 +1434,7 @@ __global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_
         return;
     }
     f32x4 acc0 = {}, acc1 = {};
-    merge_sum(part_out + (long long)row * S * kDV + lane * 8, ls, S, 0, 1, total, acc0, acc1);
+    merge_sum(part_out + (long long)row * S * kDV + lane * 8, ls, S, lane, total, acc0, acc1);
     *(bf16x8 *)o = to_bf16x8(acc0, acc1);
     if (lse && lane == 0)
         lse[row] = total;
