@@ -1808,6 +1808,51 @@ __global__ __launch_bounds__(256) void mla_head_mm(const __bf16 *__restrict__ x,
 }
 
 // ===========================================================================
+// Device-side check of the decode's data preconditions (seq_lens in range,
+// the pages a request uses in [0, num_blocks)), which the decode kernels do
+// not check: they clamp instead.  One workgroup of 16 waves; wave w checks
+// requests w, w + 16, ..., its lanes spread over the request's table entries.
+// The findings meet in LDS and one thread writes the 3-word status.
+// ===========================================================================
+__global__ __launch_bounds__(1024) void mla_check(const int32_t *__restrict__ block_table,
+                                                  const int32_t *__restrict__ seq_lens, int B,
+                                                  int MB, int P, int num_blocks,
+                                                  int32_t *__restrict__ status)
+{
+    __shared__ int bad, first, kinds;
+    if (threadIdx.x == 0) {
+        bad = 0;
+        first = 0x7FFFFFFF;
+        kinds = 0;
+    }
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int b = wave; b < B; b += 16) {
+        const long long L = seq_lens[b];
+        int kind = (L < 0 || L > (long long)MB * P) ? 1 : 0;
+        const int np = kind ? 0 : (int)((L + P - 1) / P);
+        bool bad_block = false;
+        for (int j = lane; j < np; j += 64) {
+            const int id = block_table[(long long)b * MB + j];
+            bad_block |= id < 0 || id >= num_blocks;
+        }
+        if (__any(bad_block))
+            kind |= 2;
+        if (kind && lane == 0) {
+            atomicAdd(&bad, 1);
+            atomicMin(&first, b);
+            atomicOr(&kinds, kind);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        status[0] = bad;
+        status[1] = bad ? first : -1;
+        status[2] = kinds;
+    }
+}
+
+// ===========================================================================
 // host side
 // ===========================================================================
 bool valid_shape(const mla_decode_shape_t *s, mla_status_t *err)
@@ -2108,6 +2153,22 @@ static mla_status_t launch_head_mm(int K, int M, int32_t batch, int32_t num_head
         hipLaunchKernelGGL((mla_head_mm<128, 128>), g, blk, 0, stream, xb, ts, hs, wb, ob, batch, num_heads, M);
     else
         hipLaunchKernelGGL((mla_head_mm<512, 64>), g, blk, 0, stream, xb, ts, hs, wb, ob, batch, num_heads, M);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_check_inputs(const mla_decode_shape_t *shape, const int32_t *block_table,
+                              const int32_t *seq_lens, int32_t *status, hipStream_t stream)
+{
+    if (!shape || !status)
+        return MLA_ERR_NULL_POINTER;
+    mla_status_t err = MLA_OK;
+    if (!valid_shape(shape, &err))
+        return err;
+    if (shape->batch > 0 && (!block_table || !seq_lens))
+        return MLA_ERR_NULL_POINTER;
+    hipLaunchKernelGGL(mla_check, dim3(1), dim3(1024), 0, stream, block_table, seq_lens,
+                       shape->batch, shape->max_blocks_per_seq, shape->page_size,
+                       shape->num_blocks, status);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

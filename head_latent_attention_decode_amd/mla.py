@@ -33,7 +33,7 @@ MAX_KV_SPLITS = 256
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
             "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache",
             "mla_gather_cache", "mla_merge_attn_states", "mla_decode_multi_workspace_size",
-            "mla_decode_multi", "mla_absorb_query", "mla_up_project")
+            "mla_decode_multi", "mla_absorb_query", "mla_up_project", "mla_check_inputs")
 
 
 class MLAError(RuntimeError):
@@ -92,6 +92,8 @@ def load(path: Path | str | None = None):
     lib.mla_concat_q_insert_cache.restype = ctypes.c_int
     lib.mla_concat_q_insert_cache.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp,
                                               vp, vp, vp]
+    lib.mla_check_inputs.restype = ctypes.c_int
+    lib.mla_check_inputs.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -187,6 +189,22 @@ def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_spl
                            _stream(dev))
     _check(st, "mla_decode")
     return out, lse
+
+
+def check_inputs(q, latent_cache, block_table, seq_lens, *, cache_dtype=None, status=None):
+    """Device-side check of the decode's data preconditions (mla_check_inputs):
+    returns the int32 [3] device status (count of bad requests, the lowest
+    one or -1, a bitmask: 1 = seq_len out of range, 2 = block id out of
+    range).  Asynchronous: read it when needed."""
+    shape = make_shape(q, latent_cache, block_table, cache_dtype)
+    if status is None:
+        status = torch.empty(3, dtype=torch.int32, device=q.device)
+    if (block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or
+            not block_table.is_contiguous() or not seq_lens.is_contiguous()):
+        raise ValueError("block_table and seq_lens must be contiguous int32")
+    _check(load().mla_check_inputs(ctypes.byref(shape), _ptr(block_table), _ptr(seq_lens),
+                                   _ptr(status), _stream(q.device)), "mla_check_inputs")
+    return status
 
 
 def mla_decode_multi(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,

@@ -191,6 +191,31 @@ mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
                               void *out, float *lse, hipStream_t stream);
 
 /*
+ * Device-side check of the data preconditions above, for debugging a caller:
+ * the decode entry points never read these on the host and only clamp them
+ * on the device, so a violation gives wrong numbers for that request.  This
+ * call checks them on the device, asynchronously, and reports into a status
+ * word that the caller reads when it chooses.
+ *   shape        as for mla_decode; batch, max_blocks_per_seq, page_size and
+ *                num_blocks are used (the shape must pass mla_decode's checks).
+ *   block_table  device, int32 [batch, max_blocks_per_seq].
+ *   seq_lens     device, int32 [batch].
+ *   status       device, int32 [3], overwritten (not accumulated):
+ *                status[0]  number of requests that break a precondition;
+ *                status[1]  the lowest such request, or -1;
+ *                status[2]  bit 0: some seq_len lies outside
+ *                           [0, max_blocks_per_seq * page_size];
+ *                           bit 1: some block id among a request's first
+ *                           ceil(seq_len / page_size) entries lies outside
+ *                           [0, num_blocks).
+ * One workgroup; it reads each seq_len and at most max_blocks_per_seq table
+ * entries of each request (none past the row).  Errors: missing pointers
+ * MLA_ERR_NULL_POINTER; a shape mla_decode rejects, the same status.
+ */
+mla_status_t mla_check_inputs(const mla_decode_shape_t *shape, const int32_t *block_table,
+                              const int32_t *seq_lens, int32_t *status, hipStream_t stream);
+
+/*
  * The per-head matmuls on either side of the attention (vLLM API docs,
  * mla_attention, "Data-Movement Friendly Approach (i.e. forward_mqa)":
  * ql_nope = q_nope . W_UK contracting P, then the latent output times W_UV;

@@ -137,3 +137,15 @@ def test_projection_arguments(lib):
         assert f(4, 8, FAKE, 1024, 128, FAKE, None, None) == 1
         assert f(4, 8, FAKE, 1023, 128, FAKE, FAKE, None) == 3     # stride not a multiple of 8
         assert f(4, 8, ctypes.c_void_p(0x1008), 1024, 128, FAKE, FAKE, None) == 3  # alignment
+
+
+def test_check_inputs_arguments(lib):
+    """Host-side argument checks of the device input check (fake pointers:
+    nothing is launched on an error)."""
+    f = lib.mla_check_inputs
+    shp = shape()
+    assert f(None, FAKE, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(shp), FAKE, FAKE, None, None) == 1
+    assert f(ctypes.byref(shp), None, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(shape(page_size=0)), FAKE, FAKE, FAKE, None) == 2
+    assert f(ctypes.byref(shape(num_heads=24)), FAKE, FAKE, FAKE, None) == 3
