@@ -55,6 +55,25 @@ def test_fp8_small(N, page, S):
     G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn", what=f"fp8 N={N} P={page} S={S}")
 
 
+@pytest.mark.parametrize("page", [32, 128, 256, 1024])
+@pytest.mark.parametrize("N,cache_dtype", [(16, "bf16"), (128, "bf16"), (16, "fp8_e4m3fn"),
+                                           (128, "fp8_e4m3fn")])
+def test_other_page_sizes(page, N, cache_dtype):
+    """Power-of-two page sizes the boundary accepts besides the configs' 16
+    and 64, up to its largest, 1024: lengths on both sides of a page end, and
+    at page 32 a request (5000 tokens) past the 64-page window of the
+    page-table reads."""
+    lens = [1, 100, 1023, 1024, 1025, 5000]
+    wl = W.make_workload(len(lens), N, page, lens, seed=1000 + page + N,
+                         cache_dtype=cache_dtype)
+    ref_o, ref_l = G.reference(wl)
+    for S in (1, 3):
+        _say("page", page, N, cache_dtype, S)
+        out, lse = G.run(wl, S)
+        G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype=cache_dtype,
+                what=f"P={page} N={N} {cache_dtype} S={S}")
+
+
 @pytest.mark.parametrize("N", [16, 128])
 @pytest.mark.parametrize("S", [1, 4])
 def test_zero_length_rows(N, S):
