@@ -98,7 +98,7 @@ typedef struct {
     int32_t kv_lora_rank;       /* must be 512 */
     int32_t qk_rope_head_dim;   /* must be 64 */
     int32_t num_blocks;         /* physical pages in the cache, > 0 */
-    int32_t page_size;          /* rows per page: 16, 32, 64 or 128 */
+    int32_t page_size;          /* rows per page: a power of two, 16 .. 1024 */
     int32_t max_blocks_per_seq; /* columns of block_table, > 0 */
     mla_cache_dtype_t cache_dtype;
 } mla_decode_shape_t;
