@@ -38,6 +38,8 @@
 //    bf16 output directly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 #include <stdlib.h>
 
 #include "mla_decode.h"
@@ -292,39 +294,6 @@ __device__ __forceinline__ void wait_tiles_dma(int w, int k)
         wait_k_tiles<Cfg::kDmaLo>(k);
 }
 
-// bf16 tile by direct-to-LDS loads, any tile (rows past t_end repeat row
-// t_end - 1): instruction i fills LDS chunks [64i, 64i+64) of the tile, i.e.
-// rows of the half h = i / 18 (rows 16h .. 16h+15), which lie in one page.
-// Logical chunk c of row r is stored at chunk c ^ swz(r).  Cfg::kWaves waves
-// share the 36 instructions: wave w issues w, w + kWaves, ...
-template <class Cfg>
-__device__ __forceinline__ void issue_tile_dma(const Params &p, PageWindow &win,
-                                                LDS_AS uint8_t *stage, int w, int lane, int b,
-                                                int tile_start, int t_end)
-{
-    const int last = t_end - 1;
-    const int pmask = (1 << p.page_shift) - 1;
-    const uint8_t *base[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int first = tile_start + 16 * h;
-        first = first < last ? first : last;
-        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        base[h] = p.cache + ((long long)blk << p.page_shift) * kRowBytes;
-    }
-#pragma unroll
-    for (int m = 0; m < (36 + Cfg::kWaves - 1) / Cfg::kWaves; ++m) {
-        const int i = w + Cfg::kWaves * m;
-        if (i < 36) {
-            const int q = i * 64 + lane;
-            const int r = q / kRowChunks;
-            int tok = tile_start + r;
-            tok = tok < last ? tok : last;
-            const int c = (q % kRowChunks) ^ swz(r);
-            dma16(base[i / 18] + (long long)(tok & pmask) * kRowBytes + c * 16, stage + i * 1024);
-        }
-    }
-}
 
 // ===========================================================================
 // Role-split kernel (N a multiple of 64): 64 heads per workgroup, 8 waves,
@@ -340,14 +309,14 @@ __device__ __forceinline__ void issue_tile_dma(const Params &p, PageWindow &win,
 // Iteration i of the main loop holds one barrier; after it the score waves
 // work on tile i while the value waves work on tile i-1, so on every SIMD the
 // softmax and LDS traffic of one wave overlap the MFMAs of the other.  Tiles
-// are 32 tokens of bf16 rows in a 4-stage LDS ring.
-//   bf16 cache: direct-to-LDS loads two tiles ahead (stage (i+2)%4 was last
-//     read by the value waves in iteration i-1).
-//   fp8 cache: the value waves load E4M3 bytes into registers three tiles
-//     ahead and, in iteration i, widen tile i+2 to bf16 and write it into
-//     stage (i+2)%4; each code is converted once, and the score and value
-//     loops are those of the bf16 cache.  The per-tensor scale is folded
-//     into the softmax scale and into the final normalisation.
+// are 32 tokens in a 4-stage LDS ring, loaded direct-to-LDS two tiles ahead
+// by the value waves.
+//   bf16 cache: rows of 1152 bytes.
+//   fp8 cache: the E4M3 bytes themselves (rows of 576 bytes in the first half
+//     of each stage, half the load instructions); the score waves widen their
+//     K fragments and the value waves their V^T fragments to bf16 in
+//     registers just before the MFMAs.  The per-tensor scale is folded into
+//     the softmax scale and into the final normalisation.
 // ===========================================================================
 constexpr int kWsStages = 4;
 __device__ __forceinline__ LDS_AS uint8_t *stage_of_ws(LDS_AS uint8_t *lds, int t)
@@ -362,25 +331,18 @@ constexpr int kWsLds = kWsMbuf + 2 * 64 * 4;
 static_assert(kWsLds <= 160 * 1024, "LDS budget");
 
 // Who loads the tiles (each load instruction stalls its wave for tens of
-// cycles, so where they go was set by measurement):
-//   bf16: the 4 value waves, right after the barrier: value wave v issues the
-//     direct-to-LDS instructions i = v + 4m (m < 9) of the 36 that fill a
-//     tile (16 bytes per lane).  Giving the score waves a share made every
-//     placement slower.
-//   fp8: all 8 waves: wave w issues the loads i = w + 8m of the 18 that
-//     carry a tile (16 E4M3 bytes per lane), 3 for waves 0 and 1 and 2 for
-//     the others; score waves right after the barrier, value waves after
-//     their PV MFMAs.
-// NW loading waves: bf16 instructions i = v + NW m (NW = 2 or 4 divides 36),
-// fp8 loads i = v + NW m, at most kLd8<NW> per wave.
-template <int NW>
+// cycles, so where they go was set by measurement): the 4 value waves, right
+// after the barrier, with direct-to-LDS loads of 16 bytes per lane.  A bf16
+// tile takes 36 load instructions, value wave v issuing i = v + 4m (m < 9);
+// an fp8 tile takes 18 (E4M3 bytes, widened later at the operand reads),
+// i = v + 4m < 18, i.e. 5 for waves 0 and 1 and 4 for waves 2 and 3.  Giving
+// the score waves a share made every placement slower.
+template <bool kFp8>
 struct WsDma {
-    static constexpr int kWaves = NW;
-    static constexpr int kDmaLo = 36 / NW;
-    static constexpr int kDmaHiWaves = 0;
+    static constexpr int kWaves = 4;
+    static constexpr int kDmaLo = kFp8 ? 4 : 9;
+    static constexpr int kDmaHiWaves = kFp8 ? 2 : 0;
 };
-template <int NW>
-constexpr int kLd8 = (18 + NW - 1) / NW;
 
 // One direct-to-LDS load with a wave-uniform 64-bit base in SGPRs and a
 // 32-bit per-lane byte offset (the saddr form: no per-lane 64-bit address
@@ -394,163 +356,31 @@ __device__ __forceinline__ void dma16s(const uint8_t *sbase, int voff, LDS_AS vo
                  : "memory", "m0");
 }
 
-// Per-lane source offsets of value wave v's 9 bf16 load instructions,
-// relative to the first row of the instruction's half-tile; they do not
-// depend on the tile.  Instruction i fills LDS chunks [64i, 64i+64): chunk
-// q = 64i + lane is row r = q / 72, stored position q % 72, which holds
-// logical chunk (q % 72) ^ swz(r) of the row.
-template <int NW>
-__device__ __forceinline__ void ws_dma_offsets(int v, int lane, int (&off)[36 / NW])
-{
-#pragma unroll
-    for (int m = 0; m < 36 / NW; ++m) {
-        const int i = v + NW * m;
-        const int q = i * 64 + lane;
-        const int r = q / kRowChunks;
-        const int c = (q % kRowChunks) ^ swz(r);
-        off[m] = (r - 16 * (i / 18)) * kRowBytes + c * 16;
-    }
-}
+// fp8 tiles keep their E4M3 bytes in LDS: 32 rows of 576 bytes in the first
+// half of a stage, 16-byte chunk c of row r stored at chunk c ^ swz8(r).  The
+// score waves read 8 bytes of one row per lane (16 rows of one chunk per
+// half-wave) and the value waves read V^T with ds_read_b64_tr_b8 (8 rows of
+// one chunk per 16 lanes); with the swizzle both land on distinct banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
 
-// A whole bf16 tile (tile_start + 32 <= t_end): two scalar half-tile bases,
-// then value wave v's 9 loads with the precomputed offsets.
-template <int NW>
-__device__ __forceinline__ void ws_issue_full(const Params &p, PageWindow &win,
-                                              LDS_AS uint8_t *stage, int v, int lane, int b,
-                                              int tile_start, const int (&off)[36 / NW])
-{
-    const int pmask = (1 << p.page_shift) - 1;
-    const uint8_t *base[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int first = tile_start + 16 * h;
-        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes;
-    }
-#pragma unroll
-    for (int m = 0; m < 36 / NW; ++m) {
-        const int i = v + NW * m;
-        dma16s(i < 18 ? base[0] : base[1], off[m], stage + i * 1024);
-    }
-}
-
-// fp8 cache.  Load i covers 16-byte pieces q = 64i + lane: row r = q / 36,
-// E4M3 bytes 16c .. 16c+15 (c = q % 36), i.e. the bf16 logical chunks 2c and
-// 2c+1 of the row, stored at positions (2c) ^ swz(r) and that ^ 1.  Source
-// offsets are relative to the first row of the load's half-tile (i / 9);
-// destination offsets are relative to the stage.  Every wave issues
-// kLd8<NW> loads, so that no register is loaded on one path only (the
-// compiler would then copy it, and wait for the load, at the loop's end): a
-// wave whose third load index passes 17 repeats its first load and does not
-// write it.
-template <int NW>
-__device__ __forceinline__ int ws_ld8_index(int w, int m)
-{
-    const int i = w + NW * m;
-    return i < 18 ? i : w;
-}
-template <int NW>
-__device__ __forceinline__ void ws_ld8_offsets(int w, int lane, int (&src)[kLd8<NW>],
-                                               int (&dst)[kLd8<NW>])
-{
-#pragma unroll
-    for (int m = 0; m < kLd8<NW>; ++m) {
-        const int i = ws_ld8_index<NW>(w, m);
-        const int q = i * 64 + lane;
-        const int r = q / 36, c = q % 36;
-        src[m] = (r - 16 * (i / 9)) * kRowBytes8 + c * 16;
-        dst[m] = r * kRowBytes + ((2 * c) ^ swz(r)) * 16;
-    }
-}
-
-// Raw buffer resource over the bytes from `base` (wave-uniform): the loads
-// below take a 32-bit per-lane offset against a scalar base, so no 64-bit
-// per-lane address is formed, and the compiler still tracks them.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t *base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
-}
-
-// The wave's loads of a whole fp8 tile into registers.
-template <int NW>
-__device__ __forceinline__ void ws_ld8_full(const Params &p, PageWindow &win, int w, int lane,
-                                            int b, int tile_start, const int (&src)[kLd8<NW>],
-                                            u32x4 (&r)[kLd8<NW>])
-{
-    const int pmask = (1 << p.page_shift) - 1;
-    __amdgpu_buffer_rsrc_t rs[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int first = tile_start + 16 * h;
-        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        rs[h] = rows_rsrc(p.cache +
-                          (((long long)blk << p.page_shift) + (first & pmask)) * kRowBytes8);
-    }
-#pragma unroll
-    for (int m = 0; m < kLd8<NW>; ++m) {
-        const int i = ws_ld8_index<NW>(w, m);
-        r[m] = __builtin_amdgcn_raw_buffer_load_b128(i < 9 ? rs[0] : rs[1], src[m], 0, 0);
-    }
-}
-
-// The last, partial fp8 tile: rows past t_end repeat row t_end - 1 (finite
-// values whose scores are masked), so every LDS row holds a real row.
-template <int NW>
-__device__ __forceinline__ void ws_ld8_part(const Params &p, PageWindow &win, int w, int lane,
-                                            int b, int tile_start, int t_end,
-                                            u32x4 (&r)[kLd8<NW>])
-{
-    const int last = t_end - 1;
-    const int pmask = (1 << p.page_shift) - 1;
-    __amdgpu_buffer_rsrc_t rs[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int first = tile_start + 16 * h;
-        first = first < last ? first : last;
-        const int blk = window_block(p, win, b, first >> p.page_shift, lane);
-        rs[h] = rows_rsrc(p.cache + ((long long)blk << p.page_shift) * kRowBytes8);
-    }
-#pragma unroll
-    for (int m = 0; m < kLd8<NW>; ++m) {
-        const int i = ws_ld8_index<NW>(w, m);
-        const int q = i * 64 + lane;
-        const int rr = q / 36;
-        int tok = tile_start + rr;
-        tok = tok < last ? tok : last;
-        r[m] = __builtin_amdgcn_raw_buffer_load_b128(
-            i < 9 ? rs[0] : rs[1], (tok & pmask) * kRowBytes8 + (q % 36) * 16, 0, 0);
-    }
-}
-
-// Widen the wave's loads of a tile to bf16 and write them at their swizzled
-// positions of the stage: two 16-byte writes per load.
-template <int NW>
-__device__ __forceinline__ void ws_st8(LDS_AS uint8_t *stage, int w, const int (&dst)[kLd8<NW>],
-                                       const u32x4 (&r)[kLd8<NW>])
-{
-#pragma unroll
-    for (int m = 0; m < kLd8<NW>; ++m) {
-        if (w + NW * m < 18) {
-            const u32x2 a = e4m3x4_to_bf16x4(r[m][0]);
-            const u32x2 b = e4m3x4_to_bf16x4(r[m][1]);
-            const u32x2 c = e4m3x4_to_bf16x4(r[m][2]);
-            const u32x2 d = e4m3x4_to_bf16x4(r[m][3]);
-            *(LDS_AS u32x4 *)(stage + dst[m]) = u32x4{a[0], a[1], b[0], b[1]};
-            *(LDS_AS u32x4 *)(stage + (dst[m] ^ 16)) = u32x4{c[0], c[1], d[0], d[1]};
-        }
-    }
-}
-
-// All of a wave's tile traffic: its share of the loads of each tile and,
-// for an fp8 cache, the registers that carry them to the stage.  w is the
-// wave's index among the NW loading waves.
-template <bool kFp8, int NW>
+// A value wave's tile loads.  Load instruction i fills LDS chunks
+// [64i, 64i+64) of the tile: chunk q = 64i + lane is row r = q / kChunks,
+// stored position q % kChunks, which holds logical chunk (q % kChunks) ^
+// swizzle(r) of the row.  An instruction's rows lie in one half-tile (rows
+// 16h .. 16h+15, h = i / kHalf), hence in one page; per-lane source offsets
+// are relative to the half's first row and do not depend on the tile.
+template <bool kFp8>
 struct WsLoader {
+    static constexpr int kRow = kFp8 ? kRowBytes8 : kRowBytes;
+    static constexpr int kChunks = kRow / 16;
+    static constexpr int kLoads = kT32 * kChunks / 64;     // 36 bf16, 18 fp8
+    static constexpr int kHalf = kLoads / 2;
+    static constexpr int kPerWave = (kLoads + 3) / 4;      // 9 bf16, 5 fp8
     PageWindow win;
-    int off[kFp8 ? kLd8<NW> : 36 / NW];
-    int dst[kFp8 ? kLd8<NW> : 1];
-    u32x4 rg[kFp8 ? kLd8<NW> : 1];
+    int off[kPerWave];
     int w, lane, b, t_begin, t_end;
+
+    __device__ __forceinline__ static int sw(int r) { return kFp8 ? swz8(r) : swz(r); }
 
     __device__ __forceinline__ void init(const Params &p, int w_, int lane_, int b_, int t0,
                                          int t1)
@@ -560,104 +390,126 @@ struct WsLoader {
         b = b_;
         t_begin = t0;
         t_end = t1;
-        if constexpr (kFp8)
-            ws_ld8_offsets<NW>(w, lane, off, dst);
-        else
-            ws_dma_offsets<NW>(w, lane, off);
+#pragma unroll
+        for (int m = 0; m < kPerWave; ++m) {
+            int i = w + 4 * m;
+            i = i < kLoads ? i : w;            // (a slot the wave never issues)
+            const int q = i * 64 + lane;
+            const int r = q / kChunks;
+            const int c = (q % kChunks) ^ sw(r);
+            off[m] = (r - 16 * (i / kHalf)) * kRow + c * 16;
+        }
         window_fill(p, win, b, t_begin >> p.page_shift, lane);
     }
-    // bf16: direct-to-LDS loads of tile t into its stage
+    // tile t into its stage; rows past t_end repeat row t_end - 1 (finite
+    // values whose scores are masked)
     __device__ __forceinline__ void issue(const Params &p, LDS_AS uint8_t *lds, int t)
     {
         const int ts = t_begin + t * kT32;
         LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
-        if (ts + kT32 <= t_end)
-            ws_issue_full<NW>(p, win, stage, w, lane, b, ts, off);
-        else
-            issue_tile_dma<WsDma<NW>>(p, win, stage, w, lane, b, ts, t_end);
+        const int pmask = (1 << p.page_shift) - 1;
+        const uint8_t *base[2];
+        if (ts + kT32 <= t_end) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int first = ts + 16 * h;
+                const int blk = window_block(p, win, b, first >> p.page_shift, lane);
+                base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRow;
+            }
+#pragma unroll
+            for (int m = 0; m < kPerWave; ++m) {
+                const int i = w + 4 * m;
+                if (i < kLoads)
+                    dma16s(base[i / kHalf], off[m], stage + i * 1024);
+            }
+        } else {
+            const int last = t_end - 1;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int first = ts + 16 * h;
+                first = first < last ? first : last;
+                const int blk = window_block(p, win, b, first >> p.page_shift, lane);
+                base[h] = p.cache + ((long long)blk << p.page_shift) * kRow;
+            }
+#pragma unroll
+            for (int m = 0; m < kPerWave; ++m) {
+                const int i = w + 4 * m;
+                if (i < kLoads) {
+                    const int q = i * 64 + lane;
+                    const int r = q / kChunks;
+                    int tok = ts + r;
+                    tok = tok < last ? tok : last;
+                    const int c = (q % kChunks) ^ sw(r);
+                    dma16(base[i / kHalf] + (long long)(tok & pmask) * kRow + c * 16,
+                          stage + i * 1024);
+                }
+            }
+        }
     }
-    // bf16: wait until at most k of this wave's tiles are in flight
-    __device__ __forceinline__ void wait(int k) { wait_tiles_dma<WsDma<NW>>(w, k); }
-    // fp8: loads of tile t into the registers
-    __device__ __forceinline__ void load(const Params &p, int t)
-    {
-        const int ts = t_begin + t * kT32;
-        if (ts + kT32 <= t_end)
-            ws_ld8_full<NW>(p, win, w, lane, b, ts, off, rg);
-        else
-            ws_ld8_part<NW>(p, win, w, lane, b, ts, t_end, rg);
-    }
-    // fp8: the registers, widened, into tile t's stage
-    __device__ __forceinline__ void store(LDS_AS uint8_t *lds, int t)
-    {
-        ws_st8<NW>(lds + (t & 3) * kStage32, w, dst, rg);
-    }
-    // Before the first barrier: tiles 0 and 1 issued (bf16), or written with
-    // tile 2 in the registers (fp8).
+    // before the first barrier: tiles 0 and 1
     __device__ __forceinline__ void prologue(const Params &p, LDS_AS uint8_t *lds, int ntiles)
     {
-        if constexpr (kFp8) {
-            load(p, 0);
-            store(lds, 0);
-            if (1 < ntiles) {
-                load(p, 1);
-                store(lds, 1);
-            }
-            load(p, 2 < ntiles ? 2 : ntiles - 1);
-        } else {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (t < ntiles)
-                    issue(p, lds, t);
-        }
+        for (int t = 0; t < 2; ++t)
+            if (t < ntiles)
+                issue(p, lds, t);
     }
-    // bf16, top of iteration i: this wave's loads of tile i have landed
+    // top of iteration i: this wave's loads of tile i have landed
     __device__ __forceinline__ void before_barrier(int i, int ntiles)
     {
-        if constexpr (!kFp8)
-            if (i < ntiles)
-                wait(i + 1 < ntiles ? 1 : 0);
+        if (i < ntiles)
+            wait_tiles_dma<WsDma<kFp8>>(w, i + 1 < ntiles ? 1 : 0);
     }
-    // The wave's tile traffic of iteration i: bf16 issues tile i+2 into stage
-    // (i+2)%4 (last read in iteration i-1); fp8 writes tile i+2 there from
-    // the registers and loads tile i+3 (past the last tile, the last tile
-    // again: the registers are loaded on every path).
+    // iteration i: tile i+2 into stage (i+2)%4, last read in iteration i-2
+    // (the score waves' K and the value waves' V^T prefetch of tile i-2)
     __device__ __forceinline__ void step(const Params &p, LDS_AS uint8_t *lds, int i, int ntiles)
     {
-        if constexpr (kFp8) {
-            if (i + 2 < ntiles)
-                store(lds, i + 2);
-            load(p, i + 3 < ntiles ? i + 3 : ntiles - 1);
-        } else {
-            if (i + 2 < ntiles)
-                issue(p, lds, i + 2);
-        }
+        if (i + 2 < ntiles)
+            issue(p, lds, i + 2);
     }
 };
 
+// Eight E4M3 codes widened to bf16 (exact: every E4M3 value is a bf16).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 v)
+{
+    const u32x2 lo = e4m3x4_to_bf16x4(v[0]);
+    const u32x2 hi = e4m3x4_to_bf16x4(v[1]);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // Scores of one 32-token tile for a score wave's 16 heads, lazy online
 // softmax, probabilities and rescale factor to LDS.
-template <bool kMask>
+template <bool kMask, bool kFp8>
 __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (&qf)[18],
                                               const LDS_AS uint8_t *stage, LDS_AS uint8_t *prow,
                                               LDS_AS float *arow, const int (&ko)[2], int g4,
                                               float scale_log2, int tile_start, int t_end)
 {
     constexpr int kAhead = 8;
+    // bf16: 16 bytes of a row; fp8: 8 bytes of a row (codes, widened at the MFMA)
+    using Frag = typename std::conditional<kFp8, u32x2, bf16x8>::type;
     auto kfrag = [&](int j) {
         const int k = j >> 1, tb = j & 1;
-        return *(const LDS_AS bf16x8 *)(stage + ko[k & 1] + (k >> 1) * 128 +
-                                        tb * 16 * kRowBytes);
+        if constexpr (kFp8)
+            return *(const LDS_AS u32x2 *)(stage + ko[k & 1] + (k >> 1) * 64 +
+                                           tb * 16 * kRowBytes8);
+        else
+            return *(const LDS_AS bf16x8 *)(stage + ko[k & 1] + (k >> 1) * 128 +
+                                            tb * 16 * kRowBytes);
     };
     f32x4 sc4[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-    bf16x8 kb[kAhead];
+    Frag kb[kAhead];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j)
         kb[j] = kfrag(j);
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
     for (int j = 0; j < 36; ++j) {
-        const bf16x8 a = kb[j % kAhead];
+        bf16x8 a;
+        if constexpr (kFp8)
+            a = e4m3x8_to_bf16x8(kb[j % kAhead]);
+        else
+            a = kb[j % kAhead];
         if (j + kAhead < 36)
             kb[j % kAhead] = kfrag(j + kAhead);
         sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j >> 1], sc4[j & 3], 0, 0, 0);
@@ -727,6 +579,20 @@ __device__ __forceinline__ bf16x8 ws_vfrag(const LDS_AS uint8_t *stage, const in
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// fp8: V^T fragment j of a tile as E4M3 codes, one ds_read_b64_tr_b8: lane
+// (G, jj) of 16-lane group G addresses token row 16kk + 8(G >> 1) + (jj >> 1),
+// byte 8(jj & 1) of the 16-byte chunk of columns 128vq + 32cb + 16(G & 1);
+// the transpose leaves it column jj of that chunk at 8 consecutive tokens.
+__device__ __forceinline__ u32x2 ws_vfrag8(const LDS_AS uint8_t *stage, const int (&to8)[2],
+                                           int j)
+{
+    const int cb = j & 3, kk = j >> 2;
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (LDS_AS v2i *)(stage + to8[cb & 1] + (cb >> 1) * 64 + kk * 16 * kRowBytes8));
+    return u32x2{(unsigned)r[0], (unsigned)r[1]};
+}
+
 // PV of one 32-token tile for a value wave: O^T[col][head] for its 128
 // columns (4 blocks of 32) and the 64 heads (2 blocks of 32).  vt holds the
 // tile's V^T fragments, read during the previous iteration; as the MFMAs
@@ -734,10 +600,11 @@ __device__ __forceinline__ bf16x8 ws_vfrag(const LDS_AS uint8_t *stage, const in
 // `next` (complete and visible since this iteration's barrier).  The
 // probabilities and rescale factors are read together, so the MFMAs wait
 // for one LDS round trip.
-__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], bf16x8 (&vt)[8],
+template <bool kFp8, class VFrag, class VOff>
+__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], VFrag (&vt)[8],
                                               const LDS_AS uint8_t *next,
                                               const LDS_AS uint8_t *pbuf, const LDS_AS float *abuf,
-                                              const int (&to)[2][2], int r32, int g2)
+                                              const VOff &to, int r32, int g2)
 {
     bf16x8 pf[2][2];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
 #pragma unroll
@@ -756,8 +623,14 @@ __device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], bf16x8 (&vt)[8]
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const bf16x8 a = vt[j];
-        vt[j] = ws_vfrag(next, to, j);
+        bf16x8 a;
+        if constexpr (kFp8) {
+            a = e4m3x8_to_bf16x8(vt[j]);
+            vt[j] = ws_vfrag8(next, to, j);
+        } else {
+            a = vt[j];
+            vt[j] = ws_vfrag(next, to, j);
+        }
         const int cb = j & 3, kk = j >> 2;
         o[cb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0][kk], o[cb][0], 0, 0, 0);
         o[cb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1][kk], o[cb][1], 0, 0, 0);
@@ -781,6 +654,19 @@ __device__ __forceinline__ void ws_value_offsets(int vq, int lane, int (&to)[2][
             to[h][e] = (8 * g2 + rr) * kRowBytes + ((4 * e) ^ cl ^ swz(rr)) * 16 + 8 * (j & 1) +
                        256 * vq;
     }
+}
+
+// fp8 transposed-read offsets of value wave vq (see ws_vfrag8): to8[e] for
+// 32-column blocks cb with cb & 1 == e; the swizzle of a lane's token row
+// does not depend on the 16-token step.
+__device__ __forceinline__ void ws_value_offsets8(int vq, int lane, int (&to8)[2])
+{
+    const int G = lane >> 4, jj = lane & 15;
+    const int row = 8 * (G >> 1) + (jj >> 1);
+    const int sw = swz8(row);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        to8[e] = row * kRowBytes8 + (8 * vq + ((2 * e + (G & 1)) ^ sw)) * 16 + 8 * (jj & 1);
 }
 
 // Value-wave epilogue of the role-split kernels: normalise O and write the
@@ -914,33 +800,28 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
             qf[k] = *(const bf16x8 *)(qp + 32 * k);
         int ko[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
+        for (int e = 0; e < 2; ++e) {
+            if constexpr (kFp8)
+                ko[e] = r16 * kRowBytes8 + ((2 * e + (g4 >> 1)) ^ swz8(r16)) * 16 + 8 * (g4 & 1);
+            else
+                ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
+        }
         LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * kPbufRow;
         LDS_AS float *arow = abuf + 16 * sq + r16;
         const int t_row = row_end(p, b, hg * 64 + 16 * sq, t_begin, t_chunk);
-        // fp8: the score waves take part in the tile loads (after the query
-        // loads, which complete inside the page-window fill)
-        WsLoader<kFp8, kFp8 ? 8 : 4> ld;
-        if constexpr (kFp8) {
-            ld.init(p, w, lane, b, t_begin, t_end);
-            ld.prologue(p, lds, ntiles);
-        }
         float m = -INFINITY, l = 0.f;
         for (int i = 0; i <= ntiles; ++i) {
             barrier_no_fence();
-            if constexpr (kFp8)
-                ld.step(p, lds, i, ntiles);
             if (i < ntiles) {
                 const int ts = t_begin + i * kT32;
                 if (ts + kT32 <= t_row)
-                    ws_score_tile<false>(m, l, qf, lds + (i & 3) * kStage32,
-                                         prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                         g4, scale_log2, ts, t_row);
+                    ws_score_tile<false, kFp8>(m, l, qf, lds + (i & 3) * kStage32,
+                                               prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64,
+                                               ko, g4, scale_log2, ts, t_row);
                 else
-                    ws_score_tile<true>(m, l, qf, lds + (i & 3) * kStage32,
-                                        prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64, ko,
-                                        g4, scale_log2, ts, t_row);
+                    ws_score_tile<true, kFp8>(m, l, qf, lds + (i & 3) * kStage32,
+                                              prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64,
+                                              ko, g4, scale_log2, ts, t_row);
             }
             if (i == ntiles - 1) {
                 // final (m, l) of the wave's heads, read by the value waves
@@ -963,10 +844,14 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     // (the A operand of O^T = V^T . P^T).
     const int r32 = lane & 31, g2 = lane >> 5;
     const int vq = w - 4;
-    int to[2][2];
-    ws_value_offsets(vq, lane, to);
-    WsLoader<kFp8, kFp8 ? 8 : 4> ld;
-    ld.init(p, kFp8 ? w : vq, lane, b, t_begin, t_end);
+    using VOff = typename std::conditional<kFp8, int[2], int[2][2]>::type;
+    VOff to;
+    if constexpr (kFp8)
+        ws_value_offsets8(vq, lane, to);
+    else
+        ws_value_offsets(vq, lane, to);
+    WsLoader<kFp8> ld;
+    ld.init(p, vq, lane, b, t_begin, t_end);
     ld.prologue(p, lds, ntiles);
     f32x16 o[4][2];
 #pragma unroll
@@ -976,24 +861,25 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     // and the PV of tile i-1 with its V^T from registers, reading tile i's
     // V^T for the next iteration (in the last iteration, tile i-1's again:
     // stage ntiles%4 is the epilogue's)
-    bf16x8 vt[8];
+    typename std::conditional<kFp8, u32x2, bf16x8>::type vt[8];
     for (int i = 0; i <= ntiles; ++i) {
         ld.before_barrier(i, ntiles);
         barrier_no_fence();
-        if constexpr (!kFp8)
-            ld.step(p, lds, i, ntiles);
+        ld.step(p, lds, i, ntiles);
         if (i == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vt[j] = ws_vfrag(lds, to, j);
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (kFp8)
+                    vt[j] = ws_vfrag8(lds, to, j);
+                else
+                    vt[j] = ws_vfrag(lds, to, j);
+            }
         } else {
             const int j = i - 1;
             const int nt = i < ntiles ? i : j;
-            ws_value_tile(o, vt, lds + (nt & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
-                          abuf + (j & 1) * 64, to, r32, g2);
+            ws_value_tile<kFp8>(o, vt, lds + (nt & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
+                                abuf + (j & 1) * 64, to, r32, g2);
         }
-        if constexpr (kFp8)
-            ld.step(p, lds, i, ntiles);
     }
 
     // After the last barrier the value waves read only stage (ntiles-1)%4
