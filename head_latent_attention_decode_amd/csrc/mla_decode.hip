@@ -277,7 +277,6 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(unsigned v)
 // ===========================================================================
 constexpr int kT32 = 32;                        // tokens per tile
 constexpr int kStage32 = kT32 * kRowBytes;      // 36864 bytes (bf16 tile)
-constexpr int kPbufRow = 80;                    // bytes per head row (64 + 16 pad)
 
 // Wait until this wave has at most `k` tiles (k = 0, 1, 2) of loads in flight.
 template <int n>
@@ -318,30 +317,40 @@ __device__ __forceinline__ void wait_tiles_dma(int w, int k)
 //     registers just before the MFMAs.  The per-tensor scale is folded into
 //     the softmax scale and into the final normalisation.
 // ===========================================================================
-constexpr int kWsStages = 4;
-__device__ __forceinline__ LDS_AS uint8_t *stage_of_ws(LDS_AS uint8_t *lds, int t)
-{
-    return lds + (t & (kWsStages - 1)) * kStage32;
-}
-constexpr int kWsPbufBytes = 64 * kPbufRow;                      // P of one tile
-constexpr int kWsPbuf = kWsStages * kStage32;                    // 2 P buffers
-constexpr int kWsAbuf = kWsPbuf + 2 * kWsPbufBytes;              // alpha [2][64]
-constexpr int kWsMbuf = kWsAbuf + 2 * 64 * 4;                    // m [64], l [64]
-constexpr int kWsLds = kWsMbuf + 2 * 64 * 4;
-static_assert(kWsLds <= 160 * 1024, "LDS budget");
+// Tile geometry of the role-split kernel: bf16 tiles are 32 tokens (36,864
+// bytes) in a 4-stage ring; fp8 tiles are 64 tokens of E4M3 bytes (the same
+// 36,864 bytes) in a 3-stage ring, which leaves room for the longer
+// probability rows.  A stage is free again once the barrier after its last
+// reader has passed; tiles are loaded two ahead.
+template <bool kFp8>
+struct WsGeom {
+    static constexpr int kTok = kFp8 ? 64 : 32;              // tokens per tile
+    static constexpr int kBlocks = kTok / 16;                 // 16-token blocks per tile
+    static constexpr int kStages = kFp8 ? 3 : 4;
+    static constexpr int kPRow = 2 * kTok + 16;               // bytes per head's P row (+pad)
+    static constexpr int kPBytes = 64 * kPRow;                // P of one tile
+    static constexpr int kPbuf = kStages * kStage32;          // 2 P buffers
+    static constexpr int kAbuf = kPbuf + 2 * kPBytes;         // alpha [2][64]
+    static constexpr int kMbuf = kAbuf + 2 * 64 * 4;          // m [64], l [64]
+    static constexpr int kLds = kMbuf + 2 * 64 * 4;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    __device__ __forceinline__ static LDS_AS uint8_t *stage(LDS_AS uint8_t *lds, int t)
+    {
+        return lds + (t % kStages) * kStage32;
+    }
+};
 
 // Who loads the tiles (each load instruction stalls its wave for tens of
 // cycles, so where they go was set by measurement): the 4 value waves, right
-// after the barrier, with direct-to-LDS loads of 16 bytes per lane.  A bf16
-// tile takes 36 load instructions, value wave v issuing i = v + 4m (m < 9);
-// an fp8 tile takes 18 (E4M3 bytes, widened later at the operand reads),
-// i = v + 4m < 18, i.e. 5 for waves 0 and 1 and 4 for waves 2 and 3.  Giving
-// the score waves a share made every placement slower.
-template <bool kFp8>
+// after the barrier, with direct-to-LDS loads of 16 bytes per lane.  A tile
+// takes 36 load instructions in either format (32 bf16 rows, or 64 rows of
+// E4M3 bytes, widened later at the operand reads), value wave v issuing
+// i = v + 4m (m < 9).  Giving the score waves a share made every placement
+// slower.
 struct WsDma {
     static constexpr int kWaves = 4;
-    static constexpr int kDmaLo = kFp8 ? 4 : 9;
-    static constexpr int kDmaHiWaves = kFp8 ? 2 : 0;
+    static constexpr int kDmaLo = 9;
+    static constexpr int kDmaHiWaves = 0;
 };
 
 // One direct-to-LDS load with a wave-uniform 64-bit base in SGPRs and a
@@ -366,16 +375,18 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
 // A value wave's tile loads.  Load instruction i fills LDS chunks
 // [64i, 64i+64) of the tile: chunk q = 64i + lane is row r = q / kChunks,
 // stored position q % kChunks, which holds logical chunk (q % kChunks) ^
-// swizzle(r) of the row.  An instruction's rows lie in one half-tile (rows
-// 16h .. 16h+15, h = i / kHalf), hence in one page; per-lane source offsets
-// are relative to the half's first row and do not depend on the tile.
+// swizzle(r) of the row.  An instruction's rows lie in one 16-row block
+// (rows 16h .. 16h+15, h = i / kHalf), hence in one page; per-lane source
+// offsets are relative to the block's first row and do not depend on the
+// tile.
 template <bool kFp8>
 struct WsLoader {
+    using G = WsGeom<kFp8>;
     static constexpr int kRow = kFp8 ? kRowBytes8 : kRowBytes;
     static constexpr int kChunks = kRow / 16;
-    static constexpr int kLoads = kT32 * kChunks / 64;     // 36 bf16, 18 fp8
-    static constexpr int kHalf = kLoads / 2;
-    static constexpr int kPerWave = (kLoads + 3) / 4;      // 9 bf16, 5 fp8
+    static constexpr int kLoads = G::kTok * kChunks / 64;  // 36 for either format
+    static constexpr int kHalf = kLoads / G::kBlocks;      // loads per 16 rows
+    static constexpr int kPerWave = (kLoads + 3) / 4;      // 9
     PageWindow win;
     int off[kPerWave];
     int w, lane, b, t_begin, t_end;
@@ -405,13 +416,13 @@ struct WsLoader {
     // values whose scores are masked)
     __device__ __forceinline__ void issue(const Params &p, LDS_AS uint8_t *lds, int t)
     {
-        const int ts = t_begin + t * kT32;
-        LDS_AS uint8_t *stage = lds + (t & 3) * kStage32;
+        const int ts = t_begin + t * G::kTok;
+        LDS_AS uint8_t *stage = G::stage(lds, t);
         const int pmask = (1 << p.page_shift) - 1;
-        const uint8_t *base[2];
-        if (ts + kT32 <= t_end) {
+        const uint8_t *base[G::kBlocks];
+        if (ts + G::kTok <= t_end) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < G::kBlocks; ++h) {
                 const int first = ts + 16 * h;
                 const int blk = window_block(p, win, b, first >> p.page_shift, lane);
                 base[h] = p.cache + (((long long)blk << p.page_shift) + (first & pmask)) * kRow;
@@ -425,7 +436,7 @@ struct WsLoader {
         } else {
             const int last = t_end - 1;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < G::kBlocks; ++h) {
                 int first = ts + 16 * h;
                 first = first < last ? first : last;
                 const int blk = window_block(p, win, b, first >> p.page_shift, lane);
@@ -458,10 +469,11 @@ struct WsLoader {
     __device__ __forceinline__ void before_barrier(int i, int ntiles)
     {
         if (i < ntiles)
-            wait_tiles_dma<WsDma<kFp8>>(w, i + 1 < ntiles ? 1 : 0);
+            wait_tiles_dma<WsDma>(w, i + 1 < ntiles ? 1 : 0);
     }
-    // iteration i: tile i+2 into stage (i+2)%4, last read in iteration i-2
-    // (the score waves' K and the value waves' V^T prefetch of tile i-2)
+    // iteration i: tile i+2 into its stage, last read in iteration i-2 (4
+    // stages) or i-1 (3 stages: the score waves' K and the value waves' V^T
+    // prefetch of tile i-1, both before this iteration's barrier)
     __device__ __forceinline__ void step(const Params &p, LDS_AS uint8_t *lds, int i, int ntiles)
     {
         if (i + 2 < ntiles)
@@ -477,8 +489,10 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 v)
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Scores of one 32-token tile for a score wave's 16 heads, lazy online
-// softmax, probabilities and rescale factor to LDS.
+// Scores of one tile (32 bf16 or 64 fp8 tokens) for a score wave's 16 heads,
+// lazy online softmax, probabilities and rescale factor to LDS.  MFMA j takes
+// K step k = j / NB (32 dimensions) of token block tb = j % NB (16 tokens);
+// accumulator j & 3 is tb (NB = 4) or tb + 2 (k & 1) (NB = 2, summed after).
 template <bool kMask, bool kFp8>
 __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (&qf)[18],
                                               const LDS_AS uint8_t *stage, LDS_AS uint8_t *prow,
@@ -486,10 +500,11 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
                                               float scale_log2, int tile_start, int t_end)
 {
     constexpr int kAhead = 8;
+    constexpr int NB = WsGeom<kFp8>::kBlocks, kMfma = 18 * NB;
     // bf16: 16 bytes of a row; fp8: 8 bytes of a row (codes, widened at the MFMA)
     using Frag = typename std::conditional<kFp8, u32x2, bf16x8>::type;
     auto kfrag = [&](int j) {
-        const int k = j >> 1, tb = j & 1;
+        const int k = j / NB, tb = j % NB;
         if constexpr (kFp8)
             return *(const LDS_AS u32x2 *)(stage + ko[k & 1] + (k >> 1) * 64 +
                                            tb * 16 * kRowBytes8);
@@ -504,24 +519,32 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
         kb[j] = kfrag(j);
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int j = 0; j < 36; ++j) {
+    for (int j = 0; j < kMfma; ++j) {
         bf16x8 a;
         if constexpr (kFp8)
             a = e4m3x8_to_bf16x8(kb[j % kAhead]);
         else
             a = kb[j % kAhead];
-        if (j + kAhead < 36)
+        if (j + kAhead < kMfma)
             kb[j % kAhead] = kfrag(j + kAhead);
-        sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j >> 1], sc4[j & 3], 0, 0, 0);
+        sc4[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j / NB], sc4[j & 3], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (j + kAhead < 36)
+        if (j + kAhead < kMfma)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    const f32x4 sc[2] = {sc4[0] + sc4[2], sc4[1] + sc4[3]};
-    float x[8];
+    f32x4 sc[NB];
+    if constexpr (NB == 2) {
+        sc[0] = sc4[0] + sc4[2];
+        sc[1] = sc4[1] + sc4[3];
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+            sc[tb] = sc4[tb];
+    }
+    float x[4 * NB];
     float mx = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float v = sc[tb][i] * scale_log2;
@@ -549,7 +572,7 @@ __device__ __forceinline__ void ws_score_tile(float &m, float &l, const bf16x8 (
     const float mu = m == -INFINITY ? 0.f : m;
     float lsum = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < NB; ++tb) {
         float e[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -601,17 +624,18 @@ __device__ __forceinline__ u32x2 ws_vfrag8(const LDS_AS uint8_t *stage, const in
 // probabilities and rescale factors are read together, so the MFMAs wait
 // for one LDS round trip.
 template <bool kFp8, class VFrag, class VOff>
-__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], VFrag (&vt)[8],
+__device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], VFrag (&vt)[4 * WsGeom<kFp8>::kBlocks],
                                               const LDS_AS uint8_t *next,
                                               const LDS_AS uint8_t *pbuf, const LDS_AS float *abuf,
                                               const VOff &to, int r32, int g2)
 {
-    bf16x8 pf[2][2];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
+    using G = WsGeom<kFp8>;
+    bf16x8 pf[2][G::kBlocks];   // [head block][k-step]: tokens 16kk + 8 g2 .. +8 of head 32hb + r32
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            pf[hb][kk] = *(const LDS_AS bf16x8 *)(pbuf + (32 * hb + r32) * kPbufRow +
+        for (int kk = 0; kk < G::kBlocks; ++kk)
+            pf[hb][kk] = *(const LDS_AS bf16x8 *)(pbuf + (32 * hb + r32) * G::kPRow +
                                                   (16 * kk + 8 * g2) * 2);
     const float al0 = abuf[r32], al1 = abuf[32 + r32];
     if (wave_any(al0 != 1.0f || al1 != 1.0f)) {
@@ -622,7 +646,7 @@ __device__ __forceinline__ void ws_value_tile(f32x16 (&o)[4][2], VFrag (&vt)[8],
         }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4 * G::kBlocks; ++j) {
         bf16x8 a;
         if constexpr (kFp8) {
             a = e4m3x8_to_bf16x8(vt[j]);
@@ -739,7 +763,8 @@ __device__ __forceinline__ void ws_value_epilogue(const Params &p, const f32x16 
 template <bool kDirect, bool kFp8>
 __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWsLds];
+    using G = WsGeom<kFp8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G::kLds];
 
     int b, s, hg;
     decode_work(p, b, s, hg);
@@ -770,11 +795,11 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
     }
 
     LDS_AS uint8_t *lds = AS3(smem);
-    LDS_AS uint8_t *pbuf = lds + kWsPbuf;
-    LDS_AS float *abuf = (LDS_AS float *)(lds + kWsAbuf);
-    LDS_AS float *mbuf = (LDS_AS float *)(lds + kWsMbuf);
+    LDS_AS uint8_t *pbuf = lds + G::kPbuf;
+    LDS_AS float *abuf = (LDS_AS float *)(lds + G::kAbuf);
+    LDS_AS float *mbuf = (LDS_AS float *)(lds + G::kMbuf);
 
-    const int ntiles = (t_end - t_begin + kT32 - 1) / kT32;
+    const int ntiles = (t_end - t_begin + G::kTok - 1) / G::kTok;
     float scale_log2 = p.scale_log2;
     float out_scale = 1.0f;
     if (kFp8) {
@@ -806,21 +831,21 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
             else
                 ko[e] = r16 * kRowBytes + ((4 * e) ^ g4 ^ swz(r16)) * 16;
         }
-        LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * kPbufRow;
+        LDS_AS uint8_t *prow = pbuf + (16 * sq + r16) * G::kPRow;
         LDS_AS float *arow = abuf + 16 * sq + r16;
         const int t_row = row_end(p, b, hg * 64 + 16 * sq, t_begin, t_chunk);
         float m = -INFINITY, l = 0.f;
         for (int i = 0; i <= ntiles; ++i) {
             barrier_no_fence();
             if (i < ntiles) {
-                const int ts = t_begin + i * kT32;
-                if (ts + kT32 <= t_row)
-                    ws_score_tile<false, kFp8>(m, l, qf, lds + (i & 3) * kStage32,
-                                               prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64,
+                const int ts = t_begin + i * G::kTok;
+                if (ts + G::kTok <= t_row)
+                    ws_score_tile<false, kFp8>(m, l, qf, G::stage(lds, i),
+                                               prow + (i & 1) * G::kPBytes, arow + (i & 1) * 64,
                                                ko, g4, scale_log2, ts, t_row);
                 else
-                    ws_score_tile<true, kFp8>(m, l, qf, lds + (i & 3) * kStage32,
-                                              prow + (i & 1) * kWsPbufBytes, arow + (i & 1) * 64,
+                    ws_score_tile<true, kFp8>(m, l, qf, G::stage(lds, i),
+                                              prow + (i & 1) * G::kPBytes, arow + (i & 1) * 64,
                                               ko, g4, scale_log2, ts, t_row);
             }
             if (i == ntiles - 1) {
@@ -857,18 +882,18 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
         o[cb][0] = o[cb][1] = f32x16{};
-    // iteration i: this wave's tile traffic (bf16: before, fp8: after the PV)
-    // and the PV of tile i-1 with its V^T from registers, reading tile i's
-    // V^T for the next iteration (in the last iteration, tile i-1's again:
-    // stage ntiles%4 is the epilogue's)
-    typename std::conditional<kFp8, u32x2, bf16x8>::type vt[8];
+    // iteration i: this wave's share of tile i+2's loads, then the PV of
+    // tile i-1 with its V^T from registers, reading tile i's V^T for the next
+    // iteration (in the last iteration, tile i-1's again: the stage of tile
+    // ntiles is the epilogue's)
+    typename std::conditional<kFp8, u32x2, bf16x8>::type vt[4 * G::kBlocks];
     for (int i = 0; i <= ntiles; ++i) {
         ld.before_barrier(i, ntiles);
         barrier_no_fence();
         ld.step(p, lds, i, ntiles);
         if (i == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4 * G::kBlocks; ++j) {
                 if constexpr (kFp8)
                     vt[j] = ws_vfrag8(lds, to, j);
                 else
@@ -877,15 +902,16 @@ __global__ __launch_bounds__(512, 1) void mla_split_ws(Params p)
         } else {
             const int j = i - 1;
             const int nt = i < ntiles ? i : j;
-            ws_value_tile<kFp8>(o, vt, lds + (nt & 3) * kStage32, pbuf + (j & 1) * kWsPbufBytes,
+            ws_value_tile<kFp8>(o, vt, G::stage(lds, nt), pbuf + (j & 1) * G::kPBytes,
                                 abuf + (j & 1) * 64, to, r32, g2);
         }
     }
 
-    // After the last barrier the value waves read only stage (ntiles-1)%4
-    // and no load is in flight, so stages ntiles%4 and (ntiles+1)%4 are free:
+    // After the last barrier the value waves read only the stage of tile
+    // ntiles-1 and no load is in flight, so the stages of tiles ntiles and
+    // ntiles+1 are free (with 3 or 4 stages, both differ from it):
     // value waves 0, 1 take the first, 2, 3 the second.
-    ws_value_epilogue<kDirect>(p, o, stage_of_ws(lds, ntiles + (vq >> 1)) + (vq & 1) * 32 * 528,
+    ws_value_epilogue<kDirect>(p, o, G::stage(lds, ntiles + (vq >> 1)) + (vq & 1) * 32 * 528,
                                mbuf, head0, s, vq, lane, out_scale);
 }
 
