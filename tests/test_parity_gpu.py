@@ -55,6 +55,24 @@ def test_fp8_small(N, page, S):
     G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn", what=f"fp8 N={N} P={page} S={S}")
 
 
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("S", [2, 3])
+def test_fp8_chunks_off_the_tile_grid(N, page, S):
+    """fp8 tiles are 64 tokens while chunk lengths are multiples of 32, so a
+    chunk may start half-way through a 64-token block and end in a 32-token
+    tile: 4160 and 4100 tokens at S = 2 give chunks of 2080, and 6600 at
+    S = 3 chunks of 2208."""
+    lens = [4160, 4100, 6600, 2081, 33]
+    wl = W.make_workload(len(lens), N, page, lens, seed=1100 + N + page + S,
+                         cache_dtype="fp8_e4m3fn")
+    _say("fp8 off-grid", N, page, S)
+    out, lse = G.run(wl, S)
+    ref_o, ref_l = G.reference(wl)
+    G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype="fp8_e4m3fn",
+            what=f"fp8 off-grid N={N} P={page} S={S}")
+
+
 @pytest.mark.parametrize("page", [32, 128, 256, 1024])
 @pytest.mark.parametrize("N,cache_dtype", [(16, "bf16"), (128, "bf16"), (16, "fp8_e4m3fn"),
                                            (128, "fp8_e4m3fn")])
