@@ -370,7 +370,13 @@ __device__ __forceinline__ void dma16s(const uint8_t *sbase, int voff, LDS_AS vo
 // score waves read 8 bytes of one row per lane (16 rows of one chunk per
 // half-wave) and the value waves read V^T with ds_read_b64_tr_b8 (8 rows of
 // one chunk per 16 lanes); with the swizzle both land on distinct banks.
-__device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz8(int r)
+{
+    // bit 1 from bit 2 of the row and bit 0 from bit 3: rows 4 apart differ in
+    // bit 1, so the two 16-lane groups of a transposed read (adjacent chunks
+    // of the same 8 rows) never share a bank
+    return ((r >> 1) & 2) | ((r >> 3) & 1);
+}
 
 // A value wave's tile loads.  Load instruction i fills LDS chunks
 // [64i, 64i+64) of the tile: chunk q = 64i + lane is row r = q / kChunks,
