@@ -231,11 +231,6 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b)
     return __builtin_convertvector(v, bf16x2);
 }
 
-__device__ __forceinline__ float bf16_round(float x)
-{
-    return (float)(__bf16)x;
-}
-
 // Workgroup barrier that waits only for this wave's LDS operations
 // (lgkmcnt(0): its ds_writes have landed and are visible to the other waves
 // after the barrier), not for its vector-memory operations: __syncthreads()
@@ -348,7 +343,6 @@ struct WsGeom {
 // i = v + 4m (m < 9).  Giving the score waves a share made every placement
 // slower.
 struct WsDma {
-    static constexpr int kWaves = 4;
     static constexpr int kDmaLo = 9;
     static constexpr int kDmaHiWaves = 0;
 };
@@ -1366,6 +1360,8 @@ __global__ __launch_bounds__(256) void mla_merge_cols(const float *__restrict__ 
 {
     __shared__ float red[32][65];   // [state slot][column] (+1: conflict-free column sums)
     const int row = blockIdx.x / kMergeColBlocks, cb = blockIdx.x % kMergeColBlocks;
+    if (row >= rows)   // (the grid is exactly rows * kMergeColBlocks)
+        return;
     const int t = threadIdx.x, slot = t >> 3, cg = t & 7, lane = t & 63;
     const float *ls = part_lse + (long long)row * S;
     const int c0 = cb * 64;
