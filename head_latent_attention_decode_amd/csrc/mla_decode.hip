@@ -115,12 +115,33 @@ struct Params {
 __device__ __forceinline__ int swz(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
 
 // Workgroup id -> (request, split, head group).  The hardware deals
-// consecutive workgroup ids round-robin over the 8 XCDs; when the grid is a
-// multiple of 8 the remap gives each XCD a contiguous range of work items.
+// consecutive workgroup ids round-robin over the 8 XCDs.  With S a multiple
+// of 32, each request's chunks are dealt over the XCDs in runs of 4;
+// otherwise, when the grid is a multiple of 8, each XCD gets a contiguous
+// range of work items.
 __device__ __forceinline__ void decode_work(const Params &p, int &b, int &s, int &hg)
 {
     int i = blockIdx.x;
     const int G = gridDim.x;
+    if ((p.S & 31) == 0) {
+        // S a multiple of 32: XCD x = i & 7 takes the chunks s of request b
+        // with (b + s / 4) mod 8 == x.  A request's chunks are dealt over the
+        // XCDs in runs of 4 from its own offset, so requests of ragged lengths
+        // load the XCDs evenly: contiguous request ranges per XCD left one XCD
+        // 16% above the mean on a uniform [1, 32768] batch.  Runs of 4 keep a
+        // request's query and page-table rows in one L2 for a while (runs of
+        // one were 8% slower than contiguous ranges, runs of 4 5% faster).  The
+        // head groups of a chunk stay adjacent on one XCD, so its KV rows meet
+        // in one L2.
+        const int x = i & 7, k = i >> 3;
+        const int S32 = p.S >> 5;
+        hg = k % p.HG;
+        const int k2 = k / p.HG;          // ((b * S32 + s / 32) * 4) + s % 4
+        const int r = k2 & 3, k3 = k2 >> 2;
+        b = k3 / S32;
+        s = 32 * (k3 % S32) + 4 * ((x - b) & 7) + r;
+        return;
+    }
     if ((G & 7) == 0)
         i = (i & 7) * (G >> 3) + (i >> 3);
     hg = i % p.HG;
