@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--workload", default="dsv3", choices=sorted(W.CONFIGS))
     ap.add_argument("--splits", type=int, default=None, help="override num_kv_splits")
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
-    ap.add_argument("--cpu-requests", type=int, default=8,
+    ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests in the CPU-oracle sample (0 disables it)")
     ap.add_argument("--op", default="decode",
                     choices=["decode", "insert", "gather", "merge2", "multi", "absorb", "upproj"],
