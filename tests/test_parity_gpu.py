@@ -149,11 +149,14 @@ def test_run_to_run_bitwise(N):
 
 
 @pytest.mark.parametrize("N", [16, 128])
-def test_batch_invariance(N):
-    """A request alone and the same request inside a batch give the same bits."""
-    lens = [700, 3000, 41]
+@pytest.mark.parametrize("S", [8, 32])
+def test_batch_invariance(N, S):
+    """A request alone and the same request inside a batch give the same bits
+    (at S = 32 the chunks of a request land on XCDs that depend on its index
+    in the batch)."""
+    lens = [700, 3000, 41] if S == 8 else [700, 70000, 41]
     big = W.make_workload(3, N, 64, lens, seed=700 + N)
-    ob, lb = G.run(big, 8)
+    ob, lb = G.run(big, S)
     for b in range(3):
         L = int(lens[b])
         pages = -(-L // 64)
@@ -161,8 +164,8 @@ def test_batch_invariance(N):
                          block_table=big.block_table[b:b + 1, :pages].clone().contiguous(),
                          seq_lens=big.seq_lens[b:b + 1].clone(), softmax_scale=big.softmax_scale,
                          cache_scale=big.cache_scale, cache_dtype=big.cache_dtype,
-                         num_kv_splits=8, seed=0)
-        o1, l1 = G.run(one, 8)
+                         num_kv_splits=S, seed=0)
+        o1, l1 = G.run(one, S)
         assert torch.equal(o1[0], ob[b]) and torch.equal(l1[0], lb[b]), f"request {b}"
 
 
