@@ -76,7 +76,7 @@ def _declare(lib):
     lib.oracle_merge_states.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_e4m3fn_from_float.restype = ctypes.c_uint8
     lib.oracle_e4m3fn_from_float.argtypes = [ctypes.c_float]
-    lib.oracle_gather.restype = None
+    lib.oracle_gather.restype = i32
     lib.oracle_gather.argtypes = [i32, i32, P, i32, i32, i32, ctypes.c_float, P, i32, i32, P, P,
                                   P, P]
     lib.oracle_merge_two.restype = None
@@ -234,7 +234,8 @@ def concat_insert(ql_nope, q_pe, kv_c, k_pe, slot_mapping, cache, scale_inv=1.0,
 def gather(cache, block_table, cu_seq_lens, token_to_seq, seq_starts=None, scale=1.0, lib=None):
     """Chunked-context gather (see mla_oracle.c): returns uint16 bf16 bits
     [num_tokens, D].  cache: uint16 (bf16 bits) or uint8 (E4M3FN codes)
-    [num_blocks, page_size, D]."""
+    [num_blocks, page_size, D].  Raises ValueError when a row's indices leave
+    the table or the cache (such a row has no defined value)."""
     cache = np.ascontiguousarray(cache)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     cu = np.ascontiguousarray(cu_seq_lens, dtype=np.int32)
@@ -242,11 +243,17 @@ def gather(cache, block_table, cu_seq_lens, token_to_seq, seq_starts=None, scale
     st = None if seq_starts is None else np.ascontiguousarray(seq_starts, dtype=np.int32)
     nb, P, D = cache.shape
     n = tts.shape[0]
+    if cu.shape != (bt.shape[0] + 1,) or (st is not None and st.shape != (bt.shape[0],)):
+        raise ValueError("cu_seq_lens must be [B + 1] and seq_starts [B]")
     dst = np.zeros((n, D), dtype=np.uint16)
-    (lib or load()).oracle_gather(n, D, _ptr(cache), nb, P, 1 if cache.dtype == np.uint8 else 0,
-                                  float(np.float32(scale)), _ptr(bt), bt.shape[0], bt.shape[1],
-                                  _ptr(cu), _ptr(tts), None if st is None else _ptr(st),
-                                  _ptr(dst))
+    rc = (lib or load()).oracle_gather(n, D, _ptr(cache), nb, P,
+                                       1 if cache.dtype == np.uint8 else 0,
+                                       float(np.float32(scale)), _ptr(bt), bt.shape[0],
+                                       bt.shape[1], _ptr(cu), _ptr(tts),
+                                       None if st is None else _ptr(st), _ptr(dst))
+    if rc != 0:
+        raise ValueError("oracle refused the gather: a row's owner, position, page or block "
+                         "index leaves the table or the cache")
     return dst
 
 

@@ -97,19 +97,40 @@ typedef struct {
     double softmax_scale;
 } oracle_problem;
 
-/* Element d of token t of request b, or NaN when the page table or the
- * length does not describe a valid row (the caller has already rejected
- * such inputs, so this only guards against misuse). */
-static double cache_elem(const oracle_problem *p, int b, int64_t t, int d)
+/* Value of every E4M3FN code, filled once from oracle_e4m3fn_to_double (the
+ * decoder above, pinned on the full code table), so that the inner loops
+ * look a code up instead of calling ldexp per element. */
+static double e4m3_value[256];
+static pthread_once_t e4m3_once = PTHREAD_ONCE_INIT;
+
+static void fill_e4m3_values(void)
+{
+    for (int c = 0; c < 256; ++c)
+        e4m3_value[c] = oracle_e4m3fn_to_double((uint8_t)c);
+}
+
+/* Start of token t's row of request b in the cache: logical page t / P of
+ * the request lives in physical block block_table[b][t / P], at row t mod P.
+ * The caller has already rejected tables that address rows outside the
+ * cache. */
+static const void *token_row(const oracle_problem *p, int b, int64_t t)
 {
     int64_t page = t / p->page_size;
     int64_t row = t % p->page_size;
     int32_t blk = p->block_table[(int64_t)b * p->max_blocks + page];
-    int64_t idx = ((int64_t)blk * p->page_size + row) * p->Dqk + d;
+    int64_t idx = ((int64_t)blk * p->page_size + row) * p->Dqk;
     if (p->cache_is_fp8)
-        return oracle_e4m3fn_to_double(((const uint8_t *)p->cache)[idx]) *
-               p->cache_scale;
-    return oracle_bf16_to_double(((const uint16_t *)p->cache)[idx]);
+        return (const uint8_t *)p->cache + idx;
+    return (const uint16_t *)p->cache + idx;
+}
+
+/* Element d of a row: bf16 widened exactly, or an E4M3FN code's value times
+ * the cache scale. */
+static double row_elem(const oracle_problem *p, const void *row, int d)
+{
+    if (p->cache_is_fp8)
+        return e4m3_value[((const uint8_t *)row)[d]] * p->cache_scale;
+    return oracle_bf16_to_double(((const uint16_t *)row)[d]);
 }
 
 /* Attention of query row (b, n) over tokens [t0, t1) of request b.
@@ -129,9 +150,10 @@ static void attend_span(const oracle_problem *p, int b, int n, int64_t t0,
     /* scores s_t = scale * <q, K[t]> over all Dqk columns */
     double mx = -INFINITY;
     for (int64_t t = 0; t < L; ++t) {
+        const void *krow = token_row(p, b, t0 + t);
         double dot = 0.0;
         for (int d = 0; d < p->Dqk; ++d)
-            dot += qv[d] * cache_elem(p, b, t0 + t, d);
+            dot += qv[d] * row_elem(p, krow, d);
         scores[t] = p->softmax_scale * dot;
         if (scores[t] > mx)
             mx = scores[t];
@@ -144,8 +166,9 @@ static void attend_span(const oracle_problem *p, int b, int n, int64_t t0,
     /* out = sum_t softmax_t * V[t], V = first Dv columns of the row */
     for (int64_t t = 0; t < L; ++t) {
         double w = exp(scores[t] - mx) / Z;
+        const void *vrow = token_row(p, b, t0 + t);
         for (int l = 0; l < p->Dv; ++l)
-            out[l] += w * cache_elem(p, b, t0 + t, l);
+            out[l] += w * row_elem(p, vrow, l);
     }
 }
 
@@ -265,6 +288,7 @@ int oracle_mla_decode(int B, int N, int Dqk, int Dv, int page_size,
                         cache_is_fp8, q, cache,
                         cache_is_fp8 ? (double)cache_scale : 1.0,
                         block_table, seq_lens, (double)softmax_scale};
+    pthread_once(&e4m3_once, fill_e4m3_values);
     int rc = check_problem(&p);
     if (rc)
         return rc;
@@ -311,6 +335,7 @@ int oracle_mla_attend_spans(int B, int N, int Dqk, int Dv, int page_size,
                         cache_is_fp8, q, cache,
                         cache_is_fp8 ? (double)cache_scale : 1.0,
                         block_table, seq_lens, (double)softmax_scale};
+    pthread_once(&e4m3_once, fill_e4m3_values);
     int rc = check_problem(&p);
     if (rc)
         return rc;
@@ -459,8 +484,10 @@ void oracle_concat_insert(int T, int N, int Dn, int Dr, const uint16_t *ql_nope,
  * Readings:
  *   - workspace row i belongs to request b = token_to_seq[i] and holds token
  *     seq_starts[b] + (i - cu_seq_lens[b]) of that request, found through the
- *     page table; a page-table entry outside [0, num_blocks) is clamped (the
- *     GPU side reads in bounds whatever the table holds);
+ *     page table.  A row whose owner, position, logical page or block id
+ *     falls outside the table or the cache has no defined value, so the
+ *     whole call is refused (nonzero return, nothing written), as the decode
+ *     oracle refuses such tables;
  *   - an fp8 element is dequantized as the fp32 product code_value * scale,
  *     rounded to bf16 (nearest even): where a float decides the stored bits
  *     both sides decide in fp32;
@@ -479,21 +506,42 @@ static uint16_t bf16_from_float(float f)
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
-/* dst [num_tokens, D] bf16 bits; cache [num_blocks, page_size, D] bf16 bits
- * or E4M3FN codes; block_table [B, max_blocks]. */
-void oracle_gather(int num_tokens, int D, const void *cache, int num_blocks, int page_size,
-                   int fp8, float scale, const int32_t *block_table, int B, int max_blocks,
-                   const int32_t *cu_seq_lens, const int32_t *token_to_seq,
-                   const int32_t *seq_starts, uint16_t *dst)
+/* Physical row of workspace row i, or -1 when the indices that lead to it
+ * leave the table or the cache. */
+static int64_t gather_row(int i, int num_blocks, int page_size, const int32_t *block_table,
+                          int B, int max_blocks, const int32_t *cu_seq_lens,
+                          const int32_t *token_to_seq, const int32_t *seq_starts)
 {
+    const int b = token_to_seq[i];
+    if (b < 0 || b >= B)
+        return -1;
+    const int64_t pos = (int64_t)(seq_starts ? seq_starts[b] : 0) + (i - cu_seq_lens[b]);
+    if (pos < 0)
+        return -1;
+    const int64_t pg = pos / page_size;
+    if (pg >= max_blocks)
+        return -1;
+    const int blk = block_table[(int64_t)b * max_blocks + pg];
+    if (blk < 0 || blk >= num_blocks)
+        return -1;
+    return (int64_t)blk * page_size + pos % page_size;
+}
+
+/* dst [num_tokens, D] bf16 bits; cache [num_blocks, page_size, D] bf16 bits
+ * or E4M3FN codes; block_table [B, max_blocks].  Returns 0, or 1 (and writes
+ * nothing) when some row's indices leave the table or the cache. */
+int oracle_gather(int num_tokens, int D, const void *cache, int num_blocks, int page_size,
+                  int fp8, float scale, const int32_t *block_table, int B, int max_blocks,
+                  const int32_t *cu_seq_lens, const int32_t *token_to_seq,
+                  const int32_t *seq_starts, uint16_t *dst)
+{
+    for (int i = 0; i < num_tokens; ++i)
+        if (gather_row(i, num_blocks, page_size, block_table, B, max_blocks, cu_seq_lens,
+                       token_to_seq, seq_starts) < 0)
+            return 1;
     for (int i = 0; i < num_tokens; ++i) {
-        const int b = token_to_seq[i];
-        const int64_t pos = (int64_t)(seq_starts ? seq_starts[b] : 0) + (i - cu_seq_lens[b]);
-        int64_t pg = pos / page_size;
-        pg = pg < 0 ? 0 : (pg >= max_blocks ? max_blocks - 1 : pg);
-        int blk = block_table[(int64_t)b * max_blocks + pg];
-        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-        const int64_t row = (int64_t)blk * page_size + pos % page_size;
+        const int64_t row = gather_row(i, num_blocks, page_size, block_table, B, max_blocks,
+                                       cu_seq_lens, token_to_seq, seq_starts);
         for (int d = 0; d < D; ++d) {
             if (!fp8) {
                 dst[(int64_t)i * D + d] = ((const uint16_t *)cache)[row * D + d];
@@ -503,6 +551,7 @@ void oracle_gather(int num_tokens, int D, const void *cache, int num_blocks, int
             }
         }
     }
+    return 0;
 }
 
 /* Two states per (token, head): outputs [T, N, D] as doubles, lse [N, T]. */

@@ -21,22 +21,25 @@ MUTANTS = {
     "scale_dropped": ("scores[t] = p->softmax_scale * dot;", "scores[t] = dot;"),
     "lse_base2": ("*lse = mx + log(Z);", "*lse = mx + log2(Z);"),
     "lse_without_max": ("*lse = mx + log(Z);", "*lse = log(Z);"),
-    "value_from_rope_side": ("out[l] += w * cache_elem(p, b, t0 + t, l);",
-                             "out[l] += w * cache_elem(p, b, t0 + t, l + (p->Dqk - p->Dv));"),
+    "value_from_rope_side": ("out[l] += w * row_elem(p, vrow, l);",
+                             "out[l] += w * row_elem(p, vrow, l + (p->Dqk - p->Dv));"),
     "not_normalised": ("double w = exp(scores[t] - mx) / Z;", "double w = exp(scores[t] - mx);"),
     "dot_over_latent_only": ("for (int d = 0; d < p->Dqk; ++d)\n            dot +=",
                              "for (int d = 0; d < p->Dv; ++d)\n            dot +="),
     "page_off_by_one": ("int64_t page = t / p->page_size;", "int64_t page = (t + 1) / p->page_size;"),
     "row_ignores_page": ("int64_t row = t % p->page_size;", "int64_t row = 0;"),
-    "fp8_scale_dropped": ("return oracle_e4m3fn_to_double(((const uint8_t *)p->cache)[idx]) *\n               p->cache_scale;",
-                          "return oracle_e4m3fn_to_double(((const uint8_t *)p->cache)[idx]);"),
+    "fp8_scale_dropped": ("return e4m3_value[((const uint8_t *)row)[d]] * p->cache_scale;",
+                          "return e4m3_value[((const uint8_t *)row)[d]];"),
     "fp8_subnormal_wrong": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     "fp8_bias_wrong": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     "bf16_shift_wrong": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
     "merge_weight_sign": ("double w = exp(ls[s] - total);", "double w = exp(total - ls[s]);"),
     "merge_lse_no_max": ("double total = mx + log(Z);", "double total = log(Z);"),
     "merge_empty_nan": ("if (mx == -INFINITY) {\n            lse[r] = -INFINITY;\n            continue;\n        }", ""),
-    "span_start_ignored": ("dot += qv[d] * cache_elem(p, b, t0 + t, d);", "dot += qv[d] * cache_elem(p, b, t, d);"),
+    "span_start_ignored": ("const void *krow = token_row(p, b, t0 + t);",
+                           "const void *krow = token_row(p, b, t);"),
+    "value_row_of_wrong_token": ("const void *vrow = token_row(p, b, t0 + t);",
+                                 "const void *vrow = token_row(p, b, t0 + (t + 1) % L);"),
     "max_not_tracked": ("if (scores[t] > mx)\n            mx = scores[t];", "mx = 0.0;"),
 }
 

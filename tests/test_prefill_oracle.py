@@ -76,3 +76,31 @@ def test_merge_two_neutral_symmetric_and_empty():
     e, le = oracle.merge_two(po, pl, so, pl)
     assert np.allclose(e[1:], (po[1:] + so[1:]) / 2, rtol=1e-14, atol=1e-14)
     assert np.allclose(le[:, 1:], pl[:, 1:] + np.log(2.0), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("what", ["owner", "negative_position", "page_past_table",
+                                  "block_negative", "block_past_cache"])
+def test_gather_refuses_rows_outside_the_table(what):
+    """A workspace row is a request's token found through its page table; a
+    row whose owner, position, logical page or block id leaves the table or
+    the cache has no defined value, and the oracle refuses the call instead
+    of inventing one."""
+    wl = W.make_workload(2, 16, 16, [40, 20], seed=3)
+    bt = wl.block_table.numpy().copy()
+    cu = np.array([0, 40, 60], dtype=np.int32)
+    tts = np.array([0] * 40 + [1] * 20, dtype=np.int32)
+    st = np.zeros(2, dtype=np.int32)
+    cache = _cache_np(wl)
+    oracle.gather(cache, bt, cu, tts, st)                     # the valid call is accepted
+    if what == "owner":
+        tts[5] = 2
+    elif what == "negative_position":
+        st[1] = -1
+    elif what == "page_past_table":
+        st[0] = bt.shape[1] * wl.page_size - 10               # rows run past the last column
+    elif what == "block_negative":
+        bt[1, 0] = -1
+    else:
+        bt[0, 2] = wl.cache.shape[0]
+    with pytest.raises(ValueError):
+        oracle.gather(cache, bt, cu, tts, st)
