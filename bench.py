@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the MLA decode step on one MI355X.
 
-A step is one mla_decode call over one batch of the DeepSeek-V3-shaped
-decode workload: B = 64 requests, N = 128 heads, 4096 cached tokens each,
-page size 64, bf16 query and cache, num_kv_splits = 2 (other shapes via
---workload).  The call runs the split-KV attention kernel, then the LSE
-merge kernel (one kernel when num_kv_splits == 1).  Inputs are synthetic (seeded),
-generated on the host and resident in HBM before the timed region; three
-copies of the query, cache and page table are rotated so that no step finds
-its KV rows in the 256 MB Infinity Cache left behind by the previous step.
+A step is one mla_decode call over one batch of the ragged decode workload
+(the largest of the five that fits one GPU): B = 128 requests, N = 128 heads,
+KV lengths drawn uniformly from [1, 32768] (seed 3), page size 64, bf16
+query and cache, num_kv_splits = 32.  Other workloads via --workload
+(dsv3, long_context, fp8_cache, tiny).  The call runs the split-KV attention
+kernel, then the LSE merge kernel (one kernel when num_kv_splits == 1).
+Inputs are synthetic (seeded), generated on the host and resident in HBM
+before the timed region; three copies of the query, cache and page table are
+rotated so that no step finds its KV rows in the 256 MB Infinity Cache left
+behind by the previous step.
 
 Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
 (GB/s: every KV row read once, plus q, out, lse, page-table entries and
 lengths), per-step time, TFLOP/s, the split kernel's roofline fraction
 (its duration measured with HIP events on its stream around every timed
 split launch) and the fp64 CPU oracle timed on a sample of the same
-workload.
+workload.  --op stream measures plain streaming reads of the dsv3 KV volume,
+the attainable-read reference for the decode kernels.
 """
 from __future__ import annotations
 
@@ -99,6 +102,26 @@ def measured_traffic(wl):
     return int(fields["hbm_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, n_req: int):
     """The fp64 oracle on the first n_req requests (all heads), on every host
     core this process may use.  Returns the algorithmic GB/s of that sample."""
@@ -116,6 +139,7 @@ def cpu_baseline(wl, n_req: int):
     dt = time.perf_counter() - t0
     gbs = algorithmic_bytes(sub) / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n_req} of {wl.B} requests, all {wl.N} heads, "
                       f"{int(sub.seq_lens.sum())} KV tokens, {dt:.2f} s wall"}
 
@@ -141,7 +165,7 @@ class Step:
                            vp(d["block_table"].data_ptr()), vp(d["seq_lens"].data_ptr()),
                            ctypes.c_float(wl.softmax_scale), S, vp(self.ws.data_ptr()),
                            nws * 4, vp(stream))
-        self.merge_args = (B * N, S, W.KV_LORA_RANK, vp(self.ws.data_ptr()), vp(part_lse),
+        self.merge_args = (B, N, S, W.KV_LORA_RANK, vp(self.ws.data_ptr()), vp(part_lse),
                            vp(self.out.data_ptr()), vp(self.lse.data_ptr()), vp(stream))
 
     def split(self):
@@ -160,20 +184,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="dsv3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default="ragged", choices=sorted(W.CONFIGS))
     ap.add_argument("--splits", type=int, default=None, help="override num_kv_splits")
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests in the CPU-oracle sample (0 disables it)")
     ap.add_argument("--op", default="decode",
-                    choices=["decode", "insert", "gather", "merge2", "multi", "absorb", "upproj"],
+                    choices=["decode", "insert", "gather", "merge2", "multi", "absorb", "upproj",
+                             "stream"],
                     help="decode: the attention step (default); insert: the decode step's "
                          "query concat and cache insert at the workload's B and N; gather: "
                          "the chunked-context gather of the workload's whole context; "
                          "merge2: the two-state merge of prefill partials; multi: "
                          "multi-token (speculative) decode with --qlen query rows per request; "
                          "absorb / upproj: the per-head W_UK_T / W_UV matmuls at the "
-                         "workload's B and N")
+                         "workload's B and N; stream: plain 16-byte streaming reads of the "
+                         "dsv3 KV volume (attainable HBM read bandwidth)")
     ap.add_argument("--qlen", type=int, default=4, help="query rows per request for --op multi")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a known-size kernel for "
@@ -210,6 +236,9 @@ def main():
         return
     if args.op in ("absorb", "upproj"):
         run_projection(args)
+        return
+    if args.op == "stream":
+        run_stream(args)
         return
 
     wl = W.config_workload(args.workload)
@@ -622,6 +651,46 @@ def run_projection(args):
                     f"{args.workload} shapes", "bf16", None,
                     {"tokens": B, "num_heads": N, "algorithmic_flops": flops})
     line["roofline"]["tflops"] = round(flops / (kernel_ms * 1e-3) / 1e12, 2)
+    print(json.dumps(line), flush=True)
+
+
+def run_stream(args):
+    """Attainable HBM read bandwidth: the streaming-read probe (16-byte
+    nontemporal loads, 8 in flight per thread, grid-stride) over the dsv3 KV
+    volume (64 requests x 4096 rows x 1152 bytes = 302 MB), three buffers
+    rotated so that no launch finds its data in the 256 MB Infinity Cache,
+    for a sweep of grid sizes.  The decode kernels read each KV row once, so
+    this is the ceiling their KV stream can approach on this part."""
+    from head_latent_attention_decode_amd import build as B
+    if not B.PROBE_LIB.exists():
+        raise RuntimeError(f"{B.PROBE_LIB} is missing: run __graft_entry__.build()")
+    probe = ctypes.CDLL(str(B.PROBE_LIB))
+    probe.hbm_stream_read.restype = ctypes.c_int
+    probe.hbm_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    nbytes = 64 * 4096 * W.HEAD_SIZE * 2
+    bufs = [torch.full((nbytes // 4,), c + 1, dtype=torch.int32, device=dev) for c in range(3)]
+    grids = [256, 512, 1024, 2048, 4096, 8192, 16384]
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    results = {}
+    for grid in grids:
+        calls = [(lambda b=b, g=grid: probe.hbm_stream_read(
+            ctypes.c_void_p(b.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), g,
+            ctypes.c_void_p(stream.cuda_stream))) for b in bufs]
+        ms, wall = _time_calls(calls, args.warmup, args.steps)
+        results[grid] = (ms, wall)
+    best = min(results, key=lambda g: results[g][0])
+    ms, wall = results[best]
+    line = _op_line("attainable HBM read GB/s (plain streaming read, % of HBM peak)", nbytes, ms,
+                    wall, args.steps, args.warmup, "hbm_stream_read_kernel",
+                    f"stream: 302 MB read once per launch (the dsv3 KV volume), 3 buffers "
+                    f"rotated, 16-byte nontemporal loads, best of grids {grids} "
+                    f"(256 threads each)", "u32x4 loads", None,
+                    {"best_grid": best,
+                     "gbs_by_grid": {g: round(nbytes / (results[g][0] * 1e-3) / 1e9, 1)
+                                     for g in grids}})
     print(json.dumps(line), flush=True)
 
 

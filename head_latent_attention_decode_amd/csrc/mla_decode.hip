@@ -1268,10 +1268,15 @@ __global__ __launch_bounds__(256, 1) void mla_split_h16(Params p)
 // ===========================================================================
 // LSE merge.  A state with lse = -inf carries no weight and its output is
 // not read (an empty chunk leaves it unwritten).
-//   mla_merge: one wave per row, each lane owns 8 of the 512 columns.
-//   mla_merge_cols: for few rows and many states, 8 workgroups per row, each
-//   owning 64 of the 512 columns for all states: its 256 threads are 32 state
-//   slots x 8 column groups of 8, and the slots' sums are added through LDS.
+//
+// One kernel, templated on the columns each lane owns (kCols = 8, 4, 2 or 1;
+// a wave covers 64 * kCols columns, so 512 / (64 * kCols) waves share a
+// row).  Few rows take narrow lanes so that enough waves are in flight; many
+// rows take wide ones.  Whatever the width, every output element is computed
+// the same way: each wave computes its row's total lse with the same lane
+// layout (merge_total), and the element is the FMA chain over the row's live
+// states in ascending s, starting from 0.  The bits of a row therefore depend
+// only on that row's states and S, never on how many rows share the launch.
 // ===========================================================================
 // Largest state lse of a row and the row's total lse (natural log).
 __device__ __forceinline__ void merge_total(const float *ls, int S, int lane, float &M,
@@ -1293,162 +1298,117 @@ __device__ __forceinline__ void merge_total(const float *ls, int S, int lane, fl
     total = M + __builtin_amdgcn_logf(Z) * kLn2;
 }
 
-// Weighted sum of a row's live states over this lane's 8 columns.  The live
-// states of each group of 64 are found with one ballot and taken 4 at a time,
-// so that a round's loads are all in flight before the first is used; a round
-// with fewer than 4 left repeats its last state at weight zero (a live state's
-// values are finite).  States of weight zero are never loaded.
-__device__ __forceinline__ void merge_sum(const float *po, const float *ls, int S, int lane,
-                                          float total, f32x4 &acc0, f32x4 &acc1)
+template <int kCols>
+struct MergeVec {
+    float v[kCols];
+    __device__ __forceinline__ void load(const float *p)
+    {
+        if constexpr (kCols == 8) {
+            const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = a[e];
+                v[4 + e] = b[e];
+            }
+        } else if constexpr (kCols == 4) {
+            const f32x4 a = *(const f32x4 *)p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = a[e];
+        } else if constexpr (kCols == 2) {
+            const f32x2 a = *(const f32x2 *)p;
+            v[0] = a[0];
+            v[1] = a[1];
+        } else {
+            v[0] = *p;
+        }
+    }
+};
+
+// Store kCols values as bf16 (round to nearest even) with one vector store.
+template <int kCols>
+__device__ __forceinline__ void store_bf16(__bf16 *o, const float (&a)[kCols])
 {
+    typedef __bf16 vec __attribute__((ext_vector_type(kCols == 1 ? 2 : kCols)));
+    if constexpr (kCols == 1) {
+        *o = (__bf16)a[0];
+    } else {
+        vec r;
+#pragma unroll
+        for (int e = 0; e < kCols; ++e)
+            r[e] = (__bf16)a[e];
+        *(vec *)o = r;
+    }
+}
+
+template <int kCols>
+__global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_out,
+                                                 const float *__restrict__ part_lse,
+                                                 __bf16 *__restrict__ out,
+                                                 float *__restrict__ lse, int rows, int S)
+{
+    constexpr int kWavesPerRow = kDV / (64 * kCols);
+    // states whose values are loaded per round: all of a round's loads are
+    // in flight before the first is used
+    constexpr int kBatch = 32 / kCols;
+    const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long row = wid / kWavesPerRow;
+    if (row >= rows)
+        return;
+    const int cb = (int)(wid % kWavesPerRow);
+    const int lane = threadIdx.x & 63;
+    const int col = cb * 64 * kCols + lane * kCols;
+    const float *ls = part_lse + row * S;
+    float M, total;
+    merge_total(ls, S, lane, M, total);
+    __bf16 *o = out + row * kDV + col;
+    float acc[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e)
+        acc[e] = 0.f;
+    if (M == -INFINITY) {
+        store_bf16<kCols>(o, acc);
+        if (lse && cb == 0 && lane == 0)
+            lse[row] = -INFINITY;
+        return;
+    }
+    const float *po = part_out + row * S * kDV + col;
     for (int c0 = 0; c0 < S; c0 += 64) {
         const float lv = c0 + lane < S ? ls[c0 + lane] : -INFINITY;
         unsigned long long live = __ballot(lv != -INFINITY);
         while (live) {
-            int idx[4];
-            float wgt[4];
+            int idx[kBatch];
+            float wgt[kBatch];
+            int n = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 if (live) {
                     idx[u] = __builtin_ctzll(live);
                     live &= live - 1;
                     const float l = __builtin_bit_cast(
                         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), idx[u]));
                     wgt[u] = __builtin_amdgcn_exp2f((l - total) * kLog2e);
+                    n = u + 1;
                 } else {
-                    idx[u] = idx[u > 0 ? u - 1 : 0];
+                    idx[u] = idx[0];   // (loaded, never used)
                     wgt[u] = 0.f;
                 }
             }
-            f32x4 v[4][2];
+            MergeVec<kCols> v[kBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float *src = po + (long long)(c0 + idx[u]) * kDV;
-                v[u][0] = *(const f32x4 *)src;
-                v[u][1] = *(const f32x4 *)(src + 4);
-            }
+            for (int u = 0; u < kBatch; ++u)
+                v[u].load(po + (long long)(c0 + idx[u]) * kDV);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                acc0 += wgt[u] * v[u][0];
-                acc1 += wgt[u] * v[u][1];
-            }
+            for (int u = 0; u < kBatch; ++u)
+                if (u < n)
+#pragma unroll
+                    for (int e = 0; e < kCols; ++e)
+                        acc[e] = __builtin_fmaf(wgt[u], v[u].v[e], acc[e]);
         }
     }
-}
-
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4 &a, const f32x4 &b)
-{
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = (__bf16)a[e];
-        r[4 + e] = (__bf16)b[e];
-    }
-    return r;
-}
-
-__global__ __launch_bounds__(256) void mla_merge(const float *__restrict__ part_out,
-                                                 const float *__restrict__ part_lse,
-                                                 __bf16 *__restrict__ out,
-                                                 float *__restrict__ lse, int rows, int S)
-{
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows)
-        return;
-    const int lane = threadIdx.x & 63;
-    const float *ls = part_lse + (long long)row * S;
-    float M, total;
-    merge_total(ls, S, lane, M, total);
-    __bf16 *o = out + (long long)row * kDV + lane * 8;
-    if (M == -INFINITY) {
-        *(bf16x8 *)o = bf16x8{};
-        if (lse && lane == 0)
-            lse[row] = -INFINITY;
-        return;
-    }
-    f32x4 acc0 = {}, acc1 = {};
-    merge_sum(part_out + (long long)row * S * kDV + lane * 8, ls, S, lane, total, acc0, acc1);
-    *(bf16x8 *)o = to_bf16x8(acc0, acc1);
-    if (lse && lane == 0)
+    store_bf16<kCols>(o, acc);
+    if (lse && cb == 0 && lane == 0)
         lse[row] = total;
-}
-
-constexpr int kMergeColBlocks = 8;     // 64-column blocks per row
-__global__ __launch_bounds__(256) void mla_merge_cols(const float *__restrict__ part_out,
-                                                      const float *__restrict__ part_lse,
-                                                      __bf16 *__restrict__ out,
-                                                      float *__restrict__ lse, int rows, int S)
-{
-    __shared__ float red[32][65];   // [state slot][column] (+1: conflict-free column sums)
-    const int row = blockIdx.x / kMergeColBlocks, cb = blockIdx.x % kMergeColBlocks;
-    if (row >= rows)   // (the grid is exactly rows * kMergeColBlocks)
-        return;
-    const int t = threadIdx.x, slot = t >> 3, cg = t & 7, lane = t & 63;
-    const float *ls = part_lse + (long long)row * S;
-    const int c0 = cb * 64;
-    const float *po = part_out + (long long)row * S * kDV + c0 + 8 * cg;
-    // Slot k takes states k, k + 32, ...  Its first state's values are loaded
-    // before the row total is known, so that the two load latencies overlap.
-    f32x4 v0 = {}, v1 = {};
-    if (slot < S) {
-        v0 = *(const f32x4 *)(po + (long long)slot * kDV);
-        v1 = *(const f32x4 *)(po + (long long)slot * kDV + 4);
-    }
-    // the row's total lse, computed by every wave from its lanes' states
-    float m = -INFINITY;
-    for (int s = lane; s < S; s += 64)
-        m = fmaxf(m, ls[s]);
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        m = fmaxf(m, __shfl_xor(m, d));
-    float z = 0.f;
-    if (m != -INFINITY)
-        for (int s = lane; s < S; s += 64)
-            z += __builtin_amdgcn_exp2f((ls[s] - m) * kLog2e);
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        z += __shfl_xor(z, d);
-    if (m == -INFINITY) {
-        // no live state: out = 0, lse = -inf
-        if (t < 8)
-            *(bf16x8 *)(out + (long long)row * kDV + c0 + 8 * t) = bf16x8{};
-        if (lse && cb == 0 && t == 0)
-            lse[row] = -INFINITY;
-        return;
-    }
-    const float total = m + __builtin_amdgcn_logf(z) * kLn2;
-    // A state of weight zero is dropped by a select, so an unwritten row
-    // cannot leak NaN into the sum.
-    f32x4 a0 = {}, a1 = {};
-    for (int s = slot; s < S; s += 32) {
-        if (s != slot) {
-            v0 = *(const f32x4 *)(po + (long long)s * kDV);
-            v1 = *(const f32x4 *)(po + (long long)s * kDV + 4);
-        }
-        const float l = ls[s];
-        const bool live = l != -INFINITY;
-        const float wgt = __builtin_amdgcn_exp2f((l - total) * kLog2e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a0[e] += live ? wgt * v0[e] : 0.f;
-            a1[e] += live ? wgt * v1[e] : 0.f;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        red[slot][8 * cg + e] = a0[e];
-        red[slot][8 * cg + 4 + e] = a1[e];
-    }
-    __syncthreads();
-    if (t < 64) {
-        float sum = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < 32; ++k)
-            sum += red[k][t];
-        out[(long long)row * kDV + c0 + t] = (__bf16)sum;
-        if (lse && cb == 0 && t == 0)
-            lse[row] = total;
-    }
 }
 
 // ===========================================================================
@@ -1882,21 +1842,30 @@ mla_status_t launch_split(const mla_decode_shape_t *s, const void *q, const void
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status_t launch_merge(int rows, int S, const float *part_out, const float *part_lse,
+mla_status_t launch_merge(long long rows, int S, const float *part_out, const float *part_lse,
                           void *out, float *lse, hipStream_t stream)
 {
     if (rows == 0)
         return MLA_OK;
-    // one wave per row fills the GPU once there are a few thousand rows;
-    // below that, and with enough states per row, 8 workgroups per row
-    if (rows < 4096 && S >= 8) {
-        hipLaunchKernelGGL(mla_merge_cols, dim3((unsigned)rows * kMergeColBlocks), dim3(256), 0,
-                           stream, part_out, part_lse, (__bf16 *)out, lse, rows, S);
-    } else {
-        dim3 g((unsigned)((rows + 3) / 4)), blk(256);
-        hipLaunchKernelGGL(mla_merge, g, blk, 0, stream, part_out, part_lse, (__bf16 *)out, lse,
-                           rows, S);
-    }
+    // Lanes own 8 columns (one wave per row) once there are enough rows to
+    // fill the GPU, fewer columns (more waves per row) below that.  The
+    // width changes only the launch, not the arithmetic of an element.
+    const int cols = rows >= 2048 ? 8 : rows >= 512 ? 4 : rows >= 128 ? 2 : 1;
+    const long long waves = rows * (kDV / (64 * cols));
+    const long long blocks = (waves + 3) / 4;
+    if (blocks > 0x7FFFFFFFLL)
+        return MLA_ERR_UNSUPPORTED;
+    const dim3 g((unsigned)blocks), blk(256);
+    __bf16 *o = (__bf16 *)out;
+    const int r = (int)rows;
+    if (cols == 8)
+        hipLaunchKernelGGL(mla_merge<8>, g, blk, 0, stream, part_out, part_lse, o, lse, r, S);
+    else if (cols == 4)
+        hipLaunchKernelGGL(mla_merge<4>, g, blk, 0, stream, part_out, part_lse, o, lse, r, S);
+    else if (cols == 2)
+        hipLaunchKernelGGL(mla_merge<2>, g, blk, 0, stream, part_out, part_lse, o, lse, r, S);
+    else
+        hipLaunchKernelGGL(mla_merge<1>, g, blk, 0, stream, part_out, part_lse, o, lse, r, S);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -1978,8 +1947,8 @@ mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q, const vo
                        num_kv_splits, part_out, part_lse, nullptr, nullptr, stream);
     if (err != MLA_OK)
         return err;
-    return launch_merge(shape->batch * shape->num_heads, num_kv_splits, part_out, part_lse, out,
-                        lse, stream);
+    return launch_merge((long long)shape->batch * shape->num_heads, num_kv_splits, part_out,
+                        part_lse, out, lse, stream);
 }
 
 mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
@@ -2043,17 +2012,21 @@ mla_status_t mla_decode_multi(const mla_decode_shape_t *shape, int32_t q_len, in
                        num_kv_splits, part_out, part_lse, nullptr, nullptr, stream, q_len, c);
     if (err != MLA_OK)
         return err;
-    return launch_merge((int)rows, num_kv_splits, part_out, part_lse, out, lse, stream);
+    return launch_merge((long long)rows, num_kv_splits, part_out, part_lse, out, lse, stream);
 }
 
-mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv, const float *part_out,
-                              const float *part_lse, void *out, float *lse, hipStream_t stream)
+mla_status_t mla_merge_states(int32_t batch, int32_t num_heads, int32_t S, int32_t dv,
+                              const float *part_out, const float *part_lse, void *out, float *lse,
+                              hipStream_t stream)
 {
-    if (rows < 0)
+    if (batch < 0 || num_heads < 0)
         return MLA_ERR_BAD_SHAPE;
     if (S < 1 || S > MLA_MAX_KV_SPLITS)
         return MLA_ERR_BAD_SPLITS;
     if (dv != kDV)
+        return MLA_ERR_UNSUPPORTED;
+    const long long rows = (long long)batch * num_heads;
+    if (rows > 0x7FFFFFFFLL)
         return MLA_ERR_UNSUPPORTED;
     if (rows > 0 && (!part_out || !part_lse || !out))
         return MLA_ERR_NULL_POINTER;

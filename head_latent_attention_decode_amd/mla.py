@@ -75,7 +75,7 @@ def load(path: Path | str | None = None):
     lib.mla_decode_partials.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
                                         ctypes.c_float, i32, vp, sz, vp]
     lib.mla_merge_states.restype = ctypes.c_int
-    lib.mla_merge_states.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_merge_states.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.mla_decode_multi_workspace_size.restype = sz
     lib.mla_decode_multi_workspace_size.argtypes = [ctypes.POINTER(DecodeShape), i32, i32]
     lib.mla_decode_multi.restype = ctypes.c_int
@@ -154,15 +154,28 @@ def _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale):
                     ("seq_lens", seq_lens)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if q.dtype != torch.bfloat16:
         raise ValueError("q must be bfloat16")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
-    if cache_scale is not None and (cache_scale.dtype != torch.float32 or not cache_scale.is_cuda
-                                    or cache_scale.numel() != 1):
-        raise ValueError("cache_scale must be a one-element float32 device tensor")
+    if tuple(seq_lens.shape) != (int(q.shape[0]),):
+        raise ValueError("seq_lens must hold one int32 length per request: shape [B]")
+    if cache_scale is not None and (cache_scale.dtype != torch.float32 or
+                                    cache_scale.device != q.device or cache_scale.numel() != 1):
+        raise ValueError("cache_scale must be a one-element float32 tensor on q's device")
+
+
+def _check_output(name, t, dtype, shape, device):
+    """A caller-supplied output: the library writes it in full, so its size,
+    dtype, layout and device must be exactly what the call produces."""
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or
+            not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} on {device}")
 
 
 def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
@@ -175,10 +188,13 @@ def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_spl
     dev = q.device
     if out is None:
         out = torch.empty((B, N, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    _check_output("out", out, torch.bfloat16, (B, N, KV_LORA_RANK), dev)
     if return_lse and lse is None:
         lse = torch.empty((B, N), dtype=torch.float32, device=dev)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_output("lse", lse, torch.float32, (B, N), dev)
     need = workspace_size(shape, num_kv_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -221,10 +237,13 @@ def mla_decode_multi(q, latent_cache, block_table, seq_lens, softmax_scale, num_
     dev = q.device
     if out is None:
         out = torch.empty((B, QL, N, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    _check_output("out", out, torch.bfloat16, (B, QL, N, KV_LORA_RANK), dev)
     if return_lse and lse is None:
         lse = torch.empty((B, QL, N), dtype=torch.float32, device=dev)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_output("lse", lse, torch.float32, (B, QL, N), dev)
     need = int(load().mla_decode_multi_workspace_size(ctypes.byref(shape), QL,
                                                       int(num_kv_splits)))
     if workspace is None and need > 0:
@@ -262,25 +281,31 @@ def mla_decode_partials(q, latent_cache, block_table, seq_lens, softmax_scale, n
 
 
 def mla_merge_states(part_out, part_lse, *, out=None, lse=None, return_lse=True):
-    """S-way LSE merge: part_out f32 [..., S, 512], part_lse f32 [..., S] -> (out bf16, lse f32)."""
+    """S-way LSE merge: part_out f32 [B, N, S, 512], part_lse f32 [B, N, S] ->
+    (out bf16 [B, N, 512], lse f32 [B, N] or None).  A 3-D part_out [R, S, 512]
+    is taken as B = R requests of one head each."""
     if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
         raise ValueError("partials must be float32")
     if not (part_out.is_contiguous() and part_lse.is_contiguous()):
         raise ValueError("partials must be contiguous")
-    *lead, S, dv = part_out.shape
-    if tuple(part_lse.shape) != (*lead, S):
-        raise ValueError("part_lse shape does not match part_out")
-    rows = 1
-    for d in lead:
-        rows *= d
+    if part_out.dim() not in (3, 4):
+        raise ValueError("part_out must be [B, N, S, 512] (or [R, S, 512])")
+    *lead, S, dv = (int(x) for x in part_out.shape)
+    if tuple(part_lse.shape) != (*lead, S) or part_lse.device != part_out.device:
+        raise ValueError("part_lse must be [..., S] matching part_out, on its device")
+    B, N = (lead[0], lead[1]) if len(lead) == 2 else (lead[0], 1)
+    dev = part_out.device
     if out is None:
-        out = torch.empty((*lead, dv), dtype=torch.bfloat16, device=part_out.device)
+        out = torch.empty((*lead, dv), dtype=torch.bfloat16, device=dev)
+    _check_output("out", out, torch.bfloat16, (*lead, dv), dev)
     if return_lse and lse is None:
-        lse = torch.empty(tuple(lead), dtype=torch.float32, device=part_out.device)
+        lse = torch.empty(tuple(lead), dtype=torch.float32, device=dev)
     if not return_lse:
         lse = None
-    st = load().mla_merge_states(rows, S, dv, _ptr(part_out), _ptr(part_lse), _ptr(out),
-                                 _ptr(lse), _stream(part_out.device))
+    if lse is not None:
+        _check_output("lse", lse, torch.float32, tuple(lead), dev)
+    st = load().mla_merge_states(B, N, S, dv, _ptr(part_out), _ptr(part_lse), _ptr(out),
+                                 _ptr(lse), _stream(dev))
     _check(st, "mla_merge_states")
     return out, lse
 

@@ -28,9 +28,10 @@
  * request; each chunk yields a partial (normalised output, LSE) and the
  * partials are combined with the LSE merge.  The split count is a fixed
  * argument, so the reduction order depends only on (seq_len, num_kv_splits,
- * num_heads), never on the batch or the device ("num_kv_splits: fixed split
- * count ... kept fixed by default for reproducibility across batch shapes and
- * devices", Model-Optimizer docs, mla_attention_decode, "Parameters").
+ * num_heads), never on the batch or the device: the decode API fixes the
+ * split count rather than choosing it per batch, so that results repeat
+ * whatever the batch shape or the device (Model-Optimizer docs,
+ * mla_attention_decode, "Parameters", num_kv_splits).
  * Chunk s of a request of length L covers tokens
  *     [s*C, min((s+1)*C, L)),
  *     C = max(32 * ceil(ceil(L / num_kv_splits) / 32), 2048);
@@ -178,17 +179,26 @@ mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,
  * read (it may hold anything, NaN included); a row whose states are all
  * -inf gives out = 0 and lse = -inf.
  *
- *   rows      number of rows R = B * N (>= 0).
+ *   batch     B >= 0 requests.
+ *   num_heads N >= 0 heads per request; B * N must fit an int32.
  *   S         states per row, in [1, 256].
  *   dv        row width; must be 512.
- *   part_out  device, float [R, S, dv].
- *   part_lse  device, float [R, S].
- *   out       device, bf16 [R, dv] (round to nearest even).
- *   lse       device, float [R], or NULL.
+ *   part_out  device, float [B, N, S, dv], contiguous.
+ *   part_lse  device, float [B, N, S], contiguous.
+ *   out       device, bf16 [B, N, dv] (round to nearest even).
+ *   lse       device, float [B, N], or NULL.
+ * Each (b, n) row is merged on its own: its bits depend only on its S
+ * states, not on B or N (the launch shape follows B * N, the arithmetic of
+ * an element does not).
+ * Errors: MLA_ERR_BAD_SHAPE for a negative B or N, MLA_ERR_BAD_SPLITS for S
+ * outside [1, 256], MLA_ERR_UNSUPPORTED for dv != 512 or B * N beyond int32,
+ * MLA_ERR_NULL_POINTER for a missing part_out, part_lse or out when
+ * B * N > 0.
  */
-mla_status_t mla_merge_states(int32_t rows, int32_t S, int32_t dv,
-                              const float *part_out, const float *part_lse,
-                              void *out, float *lse, hipStream_t stream);
+mla_status_t mla_merge_states(int32_t batch, int32_t num_heads, int32_t S,
+                              int32_t dv, const float *part_out,
+                              const float *part_lse, void *out, float *lse,
+                              hipStream_t stream);
 
 /*
  * Device-side check of the data preconditions above, for debugging a caller:

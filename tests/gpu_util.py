@@ -42,6 +42,25 @@ def reference(wl, rows=None):
     return oracle.mla_decode(problem(wl), rows=rows)
 
 
+def reference_all_rows(wl, requests_per_call=8, say=print):
+    """The oracle on every (b, n) row of a workload, a few requests per call
+    (all their heads), printing progress after each call so that a long run
+    keeps reporting."""
+    prob = problem(wl)
+    B, N = wl.B, wl.N
+    out = np.empty((B, N, prob.Dv))
+    lse = np.empty((B, N))
+    for b0 in range(0, B, requests_per_call):
+        bs = np.arange(b0, min(B, b0 + requests_per_call))
+        rb = np.repeat(bs, N)
+        rn = np.tile(np.arange(N), len(bs))
+        o, l = oracle.mla_decode(prob, rows=(rb, rn))
+        out[bs] = o.reshape(len(bs), N, -1)
+        lse[bs] = l.reshape(len(bs), N)
+        say(f"  oracle rows of requests {b0}..{bs[-1]} of {B} done")
+    return out, lse
+
+
 def check(out, lse, ref_out, ref_lse, lens, dtype="bf16", what=""):
     """out/lse [..., Dv]/[...] from the GPU against the oracle; lens per row."""
     tol_o, tol_l = TOL[dtype]

@@ -93,12 +93,18 @@ def test_empty_batch_is_a_noop(lib):
 
 
 def test_merge_arguments(lib):
+    """mla_merge_states(B, N, S, dv, part_out, part_lse, out, lse, stream)."""
     f = lib.mla_merge_states
-    assert f(-1, 4, 512, FAKE, FAKE, FAKE, None, None) == 2
-    assert f(8, 0, 512, FAKE, FAKE, FAKE, None, None) == 4
-    assert f(8, 4, 256, FAKE, FAKE, FAKE, None, None) == 3
-    assert f(8, 4, 512, None, FAKE, FAKE, None, None) == 1
-    assert f(0, 4, 512, None, None, None, None, None) == 0
+    assert f(-1, 4, 4, 512, FAKE, FAKE, FAKE, None, None) == 2
+    assert f(8, -1, 4, 512, FAKE, FAKE, FAKE, None, None) == 2
+    assert f(8, 4, 0, 512, FAKE, FAKE, FAKE, None, None) == 4
+    assert f(8, 4, 257, 512, FAKE, FAKE, FAKE, None, None) == 4
+    assert f(8, 4, 4, 256, FAKE, FAKE, FAKE, None, None) == 3
+    assert f(65536, 65536, 4, 512, FAKE, FAKE, FAKE, None, None) == 3   # B * N beyond int32
+    assert f(8, 4, 4, 512, None, FAKE, FAKE, None, None) == 1
+    assert f(8, 4, 4, 512, FAKE, FAKE, None, None, None) == 1
+    assert f(0, 4, 4, 512, None, None, None, None, None) == 0
+    assert f(8, 0, 4, 512, None, None, None, None, None) == 0
 
 
 def test_partials_arguments(lib):
@@ -149,3 +155,20 @@ def test_check_inputs_arguments(lib):
     assert f(ctypes.byref(shp), None, FAKE, FAKE, None) == 1
     assert f(ctypes.byref(shape(page_size=0)), FAKE, FAKE, FAKE, None) == 2
     assert f(ctypes.byref(shape(num_heads=24)), FAKE, FAKE, FAKE, None) == 3
+
+
+def test_binding_checks_caller_outputs():
+    """A caller-supplied output is written in full by the library, so the
+    binding refuses one of the wrong size, dtype or layout before any call."""
+    import torch
+    from head_latent_attention_decode_amd import mla
+    dev = torch.device("cpu")
+    good = torch.empty((2, 16, 512), dtype=torch.bfloat16)
+    mla._check_output("out", good, torch.bfloat16, (2, 16, 512), dev)
+    for bad in (torch.empty((2, 16, 511), dtype=torch.bfloat16),
+                torch.empty((2, 16, 512), dtype=torch.float32),
+                torch.empty((2, 512, 16), dtype=torch.bfloat16).transpose(1, 2)):
+        with pytest.raises(ValueError):
+            mla._check_output("out", bad, torch.bfloat16, (2, 16, 512), dev)
+    with pytest.raises(ValueError):
+        mla._check_output("lse", torch.empty(2, 15), torch.float32, (2, 16), dev)

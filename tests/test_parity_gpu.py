@@ -1,8 +1,8 @@
 """Parity of the HIP decode path with the fp64 oracle (needs an MI355X).
 
 Every call goes through the C ABI (libmla_decode.so) via the ctypes binding.
-Small cases are compared in full; the five named workloads at full size are
-compared on sampled (b, n) rows that the oracle computes one by one.
+Every case, the five named workloads at full size included, is compared with
+the oracle on every (b, n) row, element by element.
 """
 import numpy as np
 import pytest
@@ -111,11 +111,20 @@ def test_all_rows_empty():
 
 @pytest.mark.parametrize("N", [16, 128])
 def test_split_count_invariance(N):
-    lens = [2049, 517, 64]
-    wl = W.make_workload(3, N, 64, lens, seed=400 + N)
+    """out and lse do not depend on num_kv_splits (Model-Optimizer docs,
+    mla_attention_decode, "Parameters", num_kv_splits): each S is compared
+    with the oracle element by element, and with S = 1.  The 70000-token
+    request is cut into 2, 3, 4, 7, 8, 32 and 35 live chunks by S = 2, 3, 4,
+    7, 8, 32 and 64 (chunks of at least 2048 tokens), at boundaries that
+    differ from one S to the next; the 20000-token one into 2 .. 10."""
+    lens = [70000, 20000, 2049, 517, 64, 1]
+    wl = W.make_workload(len(lens), N, 64, lens, seed=400 + N)
+    _say("oracle", N)
     ref_o, ref_l = G.reference(wl)
     outs = {}
     for S in (1, 2, 3, 4, 7, 8, 32, 64):
+        C = max(32 * -(-(-(-lens[0] // S)) // 32), 2048)
+        _say("S", S, "live chunks of the longest request:", -(-lens[0] // C))
         out, lse = G.run(wl, S)
         G.check(out, lse, ref_o, ref_l, G.row_lens(wl), what=f"S={S}")
         outs[S] = (out, lse)
@@ -229,24 +238,74 @@ def test_merge_kernel_against_oracle(R, S):
     assert np.abs(lse[live] - ref_l[live]).max() <= 1e-5
 
 
-def _sample_rows(wl, n_rows, seed):
-    rng = np.random.default_rng(seed)
-    lens = wl.seq_lens.numpy()
-    bs = list(rng.integers(0, wl.B, n_rows - 4)) + [int(lens.argmax()), int(lens.argmin())] * 2
-    ns = list(rng.integers(0, wl.N, n_rows - 4)) + [0, wl.N - 1, wl.N - 1, 0]
-    return np.array(bs), np.array(ns)
-
-
 @pytest.mark.parametrize("name", ["dsv3", "ragged", "long_context", "fp8_cache"])
-def test_full_size_workloads_sampled(name):
+def test_full_size_workloads(name):
+    """Each named workload at full size, in the launch configuration the
+    benchmark times, against the oracle on every (b, n) row."""
     _say("generating", name)
     wl = W.config_workload(name)
     _say("running", name, "S =", wl.num_kv_splits)
     out, lse = G.run(wl)
-    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    rb, rn = _sample_rows(wl, 48, seed=1)
-    _say("oracle on", len(rb), "sampled rows")
-    ref_o, ref_l = G.reference(wl, rows=(rb, rn))
-    lens = wl.seq_lens.numpy()[rb]
-    e = G.check(out[rb, rn], lse[rb, rn], ref_o, ref_l, lens, dtype=wl.cache_dtype, what=name)
-    _say(name, "max errors", e)
+    _say("oracle on all", wl.B * wl.N, "rows")
+    ref_o, ref_l = G.reference_all_rows(wl, requests_per_call=8 if wl.N == 128 else 1, say=_say)
+    e = G.check(out, lse, ref_o, ref_l, G.row_lens(wl), dtype=wl.cache_dtype, what=name)
+    _say(name, "max errors (out rel, lse abs)", e)
+
+
+@pytest.mark.parametrize("S", [8, 32])
+def test_batch_invariance_across_merge_widths(S):
+    """The merge's launch follows the row count (lanes own 8, 4, 2 or 1
+    columns), its arithmetic does not: a request alone (128 rows) and inside a
+    40-request batch (5120 rows) gives the same bits."""
+    rng = np.random.default_rng(S)
+    lens = [int(x) for x in rng.integers(1, 20000, size=40)]
+    lens[0], lens[1] = 19999, 2049
+    big = W.make_workload(40, 128, 64, lens, seed=1200 + S)
+    ob, lb = G.run(big, S)
+    for b in (0, 1, 7):
+        pages = -(-lens[b] // 64)
+        one = W.Workload(name="one", q=big.q[b:b + 1].clone(), cache=big.cache,
+                         block_table=big.block_table[b:b + 1, :pages].clone().contiguous(),
+                         seq_lens=big.seq_lens[b:b + 1].clone(), softmax_scale=big.softmax_scale,
+                         cache_scale=big.cache_scale, cache_dtype=big.cache_dtype,
+                         num_kv_splits=S, seed=0)
+        o1, l1 = G.run(one, S)
+        assert torch.equal(o1[0], ob[b]) and torch.equal(l1[0], lb[b]), f"request {b}"
+
+
+def test_merge_bits_do_not_depend_on_row_count():
+    """Rows 0..4 merged alone, and among 200, 1000 and 5000 rows (each launch
+    width of the merge), give the same bits."""
+    g = torch.Generator().manual_seed(5)
+    S = 40
+    po = torch.randn(5000, S, 512, generator=g)
+    pl = torch.randn(5000, S, generator=g) * 4
+    pl[torch.rand(5000, S, generator=g) < 0.4] = -float("inf")
+    pl[3] = -float("inf")
+    po_d, pl_d = po.cuda(), pl.cuda()
+    first = None
+    for R in (5, 200, 1000, 5000):
+        out, lse = mla.mla_merge_states(po_d[:R].contiguous(), pl_d[:R].contiguous())
+        torch.cuda.synchronize()
+        got = (out[:5].cpu(), lse[:5].cpu())
+        if first is None:
+            first = got
+        assert torch.equal(got[0], first[0]) and torch.equal(got[1], first[1]), R
+    assert (first[0][3] == 0).all() and torch.isneginf(first[1][3])
+
+
+def test_binding_refuses_bad_lengths_and_outputs():
+    """seq_lens must hold B entries and caller outputs must match the call:
+    the binding raises before the library could read or write out of
+    bounds."""
+    wl = W.make_workload(2, 16, 16, [30, 5], seed=9)
+    d = G.to_device(wl)
+    args = (d["q"], d["latent_cache"], d["block_table"])
+    with pytest.raises(ValueError):
+        mla.mla_decode(*args, d["seq_lens"][:1], wl.softmax_scale, 2)
+    with pytest.raises(ValueError):
+        mla.mla_decode(*args, d["seq_lens"], wl.softmax_scale, 2,
+                       out=torch.empty((2, 16, 256), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        mla.mla_decode(*args, d["seq_lens"], wl.softmax_scale, 2,
+                       lse=torch.empty((2, 8), dtype=torch.float32, device="cuda"))
