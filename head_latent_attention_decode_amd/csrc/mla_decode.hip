@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <stdlib.h>
 
@@ -1869,6 +1870,44 @@ mla_status_t launch_merge(long long rows, int S, const float *part_out, const fl
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (mla_decode_noalloc): the split
+// partials live in this file-scope device array instead of a caller
+// workspace.  Each device that runs the library holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: its device address is fetched once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(160) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array.
+mla_status_t scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MLA_ERR_HIP;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess && slot.ptr == nullptr)
+            slot.err = hipErrorInvalidSymbol;
+    });
+    if (slot.err != hipSuccess)
+        return MLA_ERR_HIP;
+    *out = slot.ptr;
+    return MLA_OK;
+}
+
 size_t partial_bytes(const mla_decode_shape_t *s, int S)
 {
     return (size_t)s->batch * (size_t)s->num_heads * (size_t)S * (kDV + 1) * sizeof(float);
@@ -1907,6 +1946,10 @@ const char *mla_status_string(mla_status_t status)
     case MLA_ERR_BAD_SPLITS: return "MLA_ERR_BAD_SPLITS: num_kv_splits outside [1, 256]";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime rejected a launch";
+    case MLA_ERR_SCRATCH_LIMIT:
+        return "MLA_ERR_SCRATCH_LIMIT: the split partials of this call exceed the library's "
+               "static scratch (MLA_NOALLOC_SCRATCH_BYTES = 160 MiB); call mla_decode with a "
+               "workspace, or use fewer splits";
     }
     return "unknown mla_status_t";
 }
@@ -1949,6 +1992,35 @@ mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q, const vo
         return err;
     return launch_merge((long long)shape->batch * shape->num_heads, num_kv_splits, part_out,
                         part_lse, out, lse, stream);
+}
+
+mla_status_t mla_decode_noalloc(const mla_decode_shape_t *shape, const void *q,
+                                const void *latent_cache, const float *cache_scale,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                float softmax_scale, int32_t num_kv_splits, void *out, float *lse,
+                                hipStream_t stream)
+{
+    mla_status_t err = check_common(shape, q, latent_cache, cache_scale, block_table, seq_lens,
+                                    num_kv_splits);
+    if (err != MLA_OK)
+        return err;
+    if (shape->batch > 0 && !out)
+        return MLA_ERR_NULL_POINTER;
+    const size_t need = mla_decode_workspace_size(shape, num_kv_splits);
+    static_assert(kScratchBytes == MLA_NOALLOC_SCRATCH_BYTES, "documented scratch size");
+    if (need > kScratchBytes)
+        return MLA_ERR_SCRATCH_LIMIT;
+    if (shape->batch == 0)
+        return MLA_OK;
+    void *ws = nullptr;
+    if (need > 0) {
+        err = scratch_address(&ws);
+        if (err != MLA_OK)
+            return err;
+    }
+    // the same kernels as mla_decode, with the scratch as its workspace
+    return mla_decode(shape, q, latent_cache, cache_scale, block_table, seq_lens, softmax_scale,
+                      num_kv_splits, ws, need, out, lse, stream);
 }
 
 mla_status_t mla_decode_partials(const mla_decode_shape_t *shape, const void *q,

@@ -33,7 +33,10 @@ MAX_KV_SPLITS = 256
 EXPORTED = ("mla_status_string", "mla_decode_workspace_size", "mla_decode",
             "mla_decode_partials", "mla_merge_states", "mla_concat_q_insert_cache",
             "mla_gather_cache", "mla_merge_attn_states", "mla_decode_multi_workspace_size",
-            "mla_decode_multi", "mla_absorb_query", "mla_up_project", "mla_check_inputs")
+            "mla_decode_multi", "mla_absorb_query", "mla_up_project", "mla_check_inputs",
+            "mla_decode_noalloc")
+MLA_ERR_SCRATCH_LIMIT = 7
+NOALLOC_SCRATCH_BYTES = 160 << 20
 
 
 class MLAError(RuntimeError):
@@ -71,6 +74,9 @@ def load(path: Path | str | None = None):
     lib.mla_decode.restype = ctypes.c_int
     lib.mla_decode.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
                                ctypes.c_float, i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
+                                       ctypes.c_float, i32, vp, vp, vp]
     lib.mla_decode_partials.restype = ctypes.c_int
     lib.mla_decode_partials.argtypes = [ctypes.POINTER(DecodeShape), vp, vp, vp, vp, vp,
                                         ctypes.c_float, i32, vp, sz, vp]
@@ -204,6 +210,27 @@ def mla_decode(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_spl
                            int(num_kv_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
                            _stream(dev))
     _check(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_noalloc(q, latent_cache, block_table, seq_lens, softmax_scale, num_kv_splits, *,
+                       out, lse=None, cache_scale=None, cache_dtype=None):
+    """mla_decode through the allocation-free entry point: the library keeps
+    the split partials in its static device scratch (MLA_NOALLOC_SCRATCH_BYTES),
+    and the caller supplies out (bf16 [B, N, 512]) and, optionally, lse
+    (f32 [B, N]); this wrapper allocates nothing either.  Calls that overlap
+    on one device race on that scratch."""
+    _check_inputs(q, latent_cache, block_table, seq_lens, cache_scale)
+    shape = make_shape(q, latent_cache, block_table, cache_dtype)
+    B, N = shape.batch, shape.num_heads
+    _check_output("out", out, torch.bfloat16, (B, N, KV_LORA_RANK), q.device)
+    if lse is not None:
+        _check_output("lse", lse, torch.float32, (B, N), q.device)
+    st = load().mla_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(latent_cache),
+                                   _ptr(cache_scale), _ptr(block_table), _ptr(seq_lens),
+                                   float(softmax_scale), int(num_kv_splits), _ptr(out),
+                                   _ptr(lse), _stream(q.device))
+    _check(st, "mla_decode_noalloc")
     return out, lse
 
 

@@ -75,7 +75,9 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 3,    /* a shape or dtype this build does not handle */
     MLA_ERR_BAD_SPLITS = 4,     /* num_kv_splits outside [1, MLA_MAX_KV_SPLITS] */
     MLA_ERR_WORKSPACE = 5,      /* workspace missing or smaller than required */
-    MLA_ERR_HIP = 6             /* the HIP runtime rejected a launch */
+    MLA_ERR_HIP = 6,            /* the HIP runtime rejected a launch */
+    MLA_ERR_SCRATCH_LIMIT = 7   /* mla_decode_noalloc: the partials exceed
+                                   its static scratch */
 } mla_status_t;
 
 /* Cache element type.  It is explicit because the bytes alone are ambiguous:
@@ -149,6 +151,40 @@ mla_status_t mla_decode(const mla_decode_shape_t *shape, const void *q,
                         float softmax_scale, int32_t num_kv_splits,
                         void *workspace, size_t workspace_bytes, void *out,
                         float *lse, hipStream_t stream);
+
+/* Size of the static device scratch of mla_decode_noalloc: 160 MiB. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+
+/*
+ * mla_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine): the split partials go to a static device
+ * array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on until the process ends.  Its device address is looked up once per
+ * device, on that device's first call, with the device current.
+ *
+ * Arguments, checks, kernels and results are those of mla_decode (bitwise
+ * the same outputs), minus workspace and workspace_bytes.  The caller still
+ * supplies out and lse.  The stream must belong to the current device.
+ * Returns MLA_ERR_SCRATCH_LIMIT, with nothing enqueued, when
+ * mla_decode_workspace_size(shape, num_kv_splits) exceeds the scratch:
+ * B * N * S * 513 * 4 bytes must be at most 160 MiB (e.g. B = 64, N = 128
+ * up to S = 9; B = 256, N = 128 up to S = 2).  S == 1 needs no scratch.
+ *
+ * Every call on a device shares that device's one scratch array and leaves
+ * its partials there; nothing in it needs clearing between calls (every
+ * state the merge reads is written by the same call).  Calls that overlap
+ * on one device (on different streams, or from different host threads
+ * without ordering) race on the scratch and give wrong results: order them.
+ */
+mla_status_t mla_decode_noalloc(const mla_decode_shape_t *shape,
+                                const void *q, const void *latent_cache,
+                                const float *cache_scale,
+                                const int32_t *block_table,
+                                const int32_t *seq_lens, float softmax_scale,
+                                int32_t num_kv_splits, void *out, float *lse,
+                                hipStream_t stream);
 
 /*
  * The split stage of mla_decode alone: writes the per-chunk partial states
