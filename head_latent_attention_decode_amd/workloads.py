@@ -98,7 +98,7 @@ CONFIGS = {
     "long_context": dict(B=4, N=16, page_size=64, seq_lens=[131072] * 4,
                          num_kv_splits=64, cache_dtype="bf16", seed=4),
     "fp8_cache": dict(B=256, N=128, page_size=64, seq_lens=[8192] * 256,
-                      num_kv_splits=2, cache_dtype="fp8_e4m3fn", seed=5),
+                      num_kv_splits=1, cache_dtype="fp8_e4m3fn", seed=5),
 }
 
 DEFAULT_SOFTMAX_SCALE = float(np.float32(1.0 / math.sqrt(128 + 64)))
