@@ -12,12 +12,17 @@ before the timed region; three copies of the query, cache and page table are
 rotated so that no step finds its KV rows in the 256 MB Infinity Cache left
 behind by the previous step.
 
+Timing: K steps run back to back with nothing recorded between them, and
+the wall clock over them gives the step time.  Then K more steps run with HIP
+events recorded on the launch stream around each split-kernel launch, which
+gives that kernel's average launch duration for the roofline (an event
+between two launches idles the GPU for ~5 us, so these events stay out of the
+step timing).
+
 Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
 (GB/s: every KV row read once, plus q, out, lse, page-table entries and
-lengths), per-step time, TFLOP/s, the split kernel's roofline fraction
-(its duration measured with HIP events on its stream around every timed
-split launch) and the fp64 CPU oracle timed on a sample of the same
-workload.  --op stream measures plain streaming reads of the dsv3 KV volume,
+lengths), per-step time, TFLOP/s, the split kernel's roofline fraction and
+the fp64 CPU oracle timed on a sample of the same workload.  --op stream measures plain streaming reads of the dsv3 KV volume,
 the attainable-read reference for the decode kernels.
 """
 from __future__ import annotations
@@ -145,12 +150,15 @@ def cpu_baseline(wl, n_req: int):
 
 
 class Step:
-    """Pre-marshalled arguments of the two launches of one mla_decode call
-    (mla_decode_partials then mla_merge_states, exactly what mla_decode
-    enqueues), so the Python side adds as little as possible per step."""
+    """Pre-marshalled arguments of one mla_decode call (the timed step) and of
+    its split-kernel launch on its own (mla_decode_partials, for the kernel's
+    duration), so the Python side adds as little as possible per step."""
 
     def __init__(self, lib, d, wl, S, stream):
         self.lib = lib
+        self.S = S
+        # the launches below hold raw pointers: keep the tensors alive
+        self.inputs = d
         B, N = wl.B, wl.N
         self.shape = mla.make_shape(d["q"], d["latent_cache"], d["block_table"], wl.cache_dtype)
         nws = B * N * S * (W.KV_LORA_RANK + 1)
@@ -160,20 +168,35 @@ class Step:
         vp = ctypes.c_void_p
         part_lse = self.ws.data_ptr() + B * N * S * W.KV_LORA_RANK * 4
         scale_ptr = vp(d["cache_scale"].data_ptr()) if d["cache_scale"] is not None else None
-        self.split_args = (ctypes.byref(self.shape), vp(d["q"].data_ptr()),
-                           vp(d["latent_cache"].data_ptr()), scale_ptr,
-                           vp(d["block_table"].data_ptr()), vp(d["seq_lens"].data_ptr()),
-                           ctypes.c_float(wl.softmax_scale), S, vp(self.ws.data_ptr()),
-                           nws * 4, vp(stream))
+        inputs = (ctypes.byref(self.shape), vp(d["q"].data_ptr()),
+                  vp(d["latent_cache"].data_ptr()), scale_ptr,
+                  vp(d["block_table"].data_ptr()), vp(d["seq_lens"].data_ptr()),
+                  ctypes.c_float(wl.softmax_scale), S)
+        self.decode_args = inputs + (vp(self.ws.data_ptr()), nws * 4, vp(self.out.data_ptr()),
+                                     vp(self.lse.data_ptr()), vp(stream))
+        self.split_args = inputs + (vp(self.ws.data_ptr()), nws * 4, vp(stream))
         self.merge_args = (B, N, S, W.KV_LORA_RANK, vp(self.ws.data_ptr()), vp(part_lse),
                            vp(self.out.data_ptr()), vp(self.lse.data_ptr()), vp(stream))
 
+    def decode(self):
+        """One step: the whole mla_decode call (split kernel, then the merge;
+        one direct kernel when S == 1)."""
+        st = self.lib.mla_decode(*self.decode_args)
+        if st != 0:
+            raise mla.MLAError(st, "mla_decode")
+
     def split(self):
+        """The dominant kernel alone: the kernel mla_decode launches first (at
+        S == 1 the only one)."""
+        if self.S == 1:
+            return self.decode()
         st = self.lib.mla_decode_partials(*self.split_args)
         if st != 0:
             raise mla.MLAError(st, "mla_decode_partials")
 
     def merge(self):
+        if self.S == 1:
+            return
         st = self.lib.mla_merge_states(*self.merge_args)
         if st != 0:
             raise mla.MLAError(st, "mla_merge_states")
@@ -258,34 +281,38 @@ def main():
     # untimed warmup, long enough for the GPU clocks to reach their steady
     # state under this load
     for i in range(args.warmup):
-        st = copies[i % len(copies)]
-        st.split()
-        st.merge()
+        copies[i % len(copies)].decode()
     torch.cuda.synchronize()
 
+    # The timed region: K whole steps back to back, nothing between them (an
+    # event recorded between two launches idles the GPU for ~5 us).
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    last = torch.cuda.Event(enable_timing=True)
+    first.record(stream)
+    for i in range(K):
+        copies[i % len(copies)].decode()
+    last.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    gpu_ms_per_step = first.elapsed_time(last) / K
+
+    # The dominant kernel's launch duration: K more steps, each with HIP events
+    # recorded on the launch stream around its split-kernel launch (the merge
+    # follows outside the events).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
     for i in range(K):
         st = copies[i % len(copies)]
         ev[i][0].record(stream)
         st.split()
         ev[i][1].record(stream)
         st.merge()
-    last.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    ms_per_step = wall * 1e3 / K
-    # event time of the split kernel alone, on its stream, every timed step
     split_each = np.array([a.elapsed_time(b) for a, b in ev])
     split_ms = float(split_each.mean())
-    # each step on the GPU's own clock: from one split's start to the next
-    step_each = np.array([ev[i][0].elapsed_time(ev[i + 1][0]) for i in range(K - 1)] +
-                         [ev[K - 1][0].elapsed_time(last)])
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -320,8 +347,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "step_us_p10_p50_p90": [round(float(v) * 1e3, 2)
-                                for v in np.percentile(step_each, [10, 50, 90])],
+        "gpu_us_per_step": round(gpu_ms_per_step * 1e3, 2),
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "decode_tokens_per_s": round(wl.B / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(int(lens.sum()) / (ms_per_step * 1e-3), 1),
@@ -418,21 +444,27 @@ def run_insert(args):
 
 
 def _time_calls(calls, warmup, steps):
-    """Warm up, then time `steps` calls (rotating over `calls`) with HIP events
-    around each launch on the current stream; returns (mean event ms, wall s)."""
+    """Warm up, time `steps` calls (rotating over `calls`) back to back on the
+    wall clock, then `steps` more with HIP events around each launch on the
+    current stream.  Returns (mean event ms per call, wall s of the first
+    pass); the events stay out of the wall-clock pass because each one idles
+    the GPU for a few microseconds."""
     stream = torch.cuda.current_stream(torch.device("cuda:0"))
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         calls[i % len(calls)]()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
 
 
@@ -668,6 +700,9 @@ def run_stream(args):
     probe.hbm_stream_read.restype = ctypes.c_int
     probe.hbm_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
+    probe.hbm_stream_read_lds.restype = ctypes.c_int
+    probe.hbm_stream_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     nbytes = 64 * 4096 * W.HEAD_SIZE * 2
     bufs = [torch.full((nbytes // 4,), c + 1, dtype=torch.int32, device=dev) for c in range(3)]
@@ -681,6 +716,15 @@ def run_stream(args):
             ctypes.c_void_p(stream.cuda_stream))) for b in bufs]
         ms, wall = _time_calls(calls, args.warmup, args.steps)
         results[grid] = (ms, wall)
+    # the decode kernels' load path: direct-to-LDS, 256 workgroups (one per
+    # CU) with 1, 2 or 4 streaming waves
+    lds_gbs = {}
+    for active in (1, 2, 4):
+        calls = [(lambda b=b, a=active: probe.hbm_stream_read_lds(
+            ctypes.c_void_p(b.data_ptr()), nbytes, 256, a,
+            ctypes.c_void_p(stream.cuda_stream))) for b in bufs]
+        lms, _ = _time_calls(calls, args.warmup, args.steps)
+        lds_gbs[f"{active}_waves_per_cu"] = round(nbytes / (lms * 1e-3) / 1e9, 1)
     best = min(results, key=lambda g: results[g][0])
     ms, wall = results[best]
     line = _op_line("attainable HBM read GB/s (plain streaming read, % of HBM peak)", nbytes, ms,
@@ -690,7 +734,8 @@ def run_stream(args):
                     f"(256 threads each)", "u32x4 loads", None,
                     {"best_grid": best,
                      "gbs_by_grid": {g: round(nbytes / (results[g][0] * 1e-3) / 1e9, 1)
-                                     for g in grids}})
+                                     for g in grids},
+                     "direct_to_lds_gbs": lds_gbs})
     print(json.dumps(line), flush=True)
 
 

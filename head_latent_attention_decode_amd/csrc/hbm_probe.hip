@@ -3,11 +3,17 @@
 // decode path; the benchmark uses it to put the decode kernels' bandwidth
 // next to what plain reads achieve on the same part.
 //
-// Each thread reads 16-byte chunks with nontemporal loads (the data is used
-// once), kUnroll chunks in flight per loop trip, grid-stride over the buffer,
-// and folds them into a register.  The register is stored only if it equals
-// a value no real buffer produces, so the loads cannot be optimised away and
-// the kernel writes (in practice) nothing.
+// Plain reads: each thread reads 16-byte chunks with nontemporal loads (the
+// data is used once), kUnroll chunks in flight per loop trip, grid-stride
+// over the buffer, and folds them into a register.  The register is stored
+// only if it equals a value no real buffer produces, so the loads cannot be
+// optimised away and the kernel writes (in practice) nothing.
+//
+// Direct-to-LDS reads: the path the decode kernels stage their KV tiles
+// through (global_load_lds_dwordx4, 1 KB per wave instruction, no register
+// round trip).  `active` waves of each 256-thread workgroup stream
+// interleaved 1 KB pieces into a private 16-slot LDS ring, at most 16 in
+// flight per wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +45,29 @@ __global__ __launch_bounds__(kThreads) void hbm_stream_read_kernel(
         sink[blockIdx.x] = x;
 }
 
+__global__ __launch_bounds__(kThreads) void hbm_stream_read_lds_kernel(
+    const uint8_t *__restrict__ src, long long n_pieces, int active)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * 16 * 1024];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (w >= active)
+        return;
+    const long long waves = (long long)gridDim.x * active;
+    int slot = 0;
+    for (long long k = (long long)blockIdx.x * active + w; k < n_pieces; k += waves) {
+        const unsigned m0 = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)(ring + w * 16384 + (slot & 15) * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(m0), "v"(src + k * 1024 + lane * 16)
+                     : "memory", "m0");
+        // a slot is written again 16 loads later, after its load has landed
+        if ((++slot & 7) == 0)
+            __builtin_amdgcn_s_waitcnt((8 & 15) | (0x7 << 4) | (0xF << 8));   // vmcnt(8)
+    }
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));                     // vmcnt(0)
+}
+
 } // namespace
 
 extern "C" {
@@ -53,6 +82,19 @@ int hbm_stream_read(const void *src, size_t bytes, unsigned *sink, int grid, hip
         return 1;
     hipLaunchKernelGGL(hbm_stream_read_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const u32x4 *)src, (long long)(bytes / 16), sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Read `bytes` (a multiple of 1024, 16-byte aligned) at `src` once into LDS
+// with direct-to-LDS loads: `grid` workgroups, `active` (1 .. 4) streaming
+// waves each.  Returns 0 after enqueuing on `stream`, 1 for bad arguments, 2
+// if the launch failed.
+int hbm_stream_read_lds(const void *src, size_t bytes, int grid, int active, hipStream_t stream)
+{
+    if (!src || grid < 1 || active < 1 || active > 4 || (bytes & 1023) || ((uintptr_t)src & 15))
+        return 1;
+    hipLaunchKernelGGL(hbm_stream_read_lds_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const uint8_t *)src, (long long)(bytes / 1024), active);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
