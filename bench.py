@@ -13,11 +13,11 @@ rotated so that no step finds its KV rows in the 256 MB Infinity Cache left
 behind by the previous step.
 
 Timing: K steps run back to back with nothing recorded between them, and
-the wall clock over them gives the step time.  Then K more steps run with HIP
-events recorded on the launch stream around each split-kernel launch, which
-gives that kernel's average launch duration for the roofline (an event
-between two launches idles the GPU for ~5 us, so these events stay out of the
-step timing).
+the wall clock over them gives the step time.  Then the split kernel runs K
+more times alone, back to back in groups of 20 with HIP events recorded on the
+launch stream around each group, which gives its average launch duration for
+the roofline (an event between two launches idles the GPU for ~5 us, so no
+event sits between two timed launches).
 
 Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
 (GB/s: every KV row read once, plus q, out, lse, page-table entries and
@@ -46,6 +46,7 @@ from head_latent_attention_decode_amd import mla  # noqa: E402
 from head_latent_attention_decode_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+KERNEL_GROUP = 20               # launches per event pair when timing one kernel
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = ("decode attention GB/s and TFLOP/s (% of HBM/MFMA roofline); "
           "µs per B×N×Skv step")
@@ -299,19 +300,23 @@ def main():
     ms_per_step = wall * 1e3 / K
     gpu_ms_per_step = first.elapsed_time(last) / K
 
-    # The dominant kernel's launch duration: K more steps, each with HIP events
-    # recorded on the launch stream around its split-kernel launch (the merge
-    # follows outside the events).
+    # The dominant kernel's launch duration: K more launches of it alone, back to
+    # back in groups of KERNEL_GROUP with HIP events recorded on the launch
+    # stream around each group (an event pair around every launch would add
+    # its own idle time to each), rotating over the copies; the merges follow
+    # each group outside the events.
+    n_groups = max(1, K // KERNEL_GROUP)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    for i in range(K):
-        st = copies[i % len(copies)]
-        ev[i][0].record(stream)
-        st.split()
-        ev[i][1].record(stream)
-        st.merge()
+          for _ in range(n_groups)]
+    for g in range(n_groups):
+        ev[g][0].record(stream)
+        for i in range(KERNEL_GROUP):
+            copies[i % len(copies)].split()
+        ev[g][1].record(stream)
+        for st in copies:
+            st.merge()
     torch.cuda.synchronize()
-    split_each = np.array([a.elapsed_time(b) for a, b in ev])
+    split_each = np.array([a.elapsed_time(b) / KERNEL_GROUP for a, b in ev])
     split_ms = float(split_each.mean())
     nbytes = algorithmic_bytes(wl)
     flops = algorithmic_flops(wl)
@@ -333,8 +338,8 @@ def main():
     roof["traffic"] = measured_traffic(wl)
     roof["kernel"] = split_kernel_name(wl)
     roof["kernel_ms"] = round(split_ms, 5)
-    roof["kernel_us_p10_p50_p90"] = [round(float(v) * 1e3, 2)
-                                     for v in np.percentile(split_each, [10, 50, 90])]
+    roof["kernel_us_p10_p50_p90_of_groups"] = [round(float(v) * 1e3, 2)
+                                               for v in np.percentile(split_each, [10, 50, 90])]
 
     cpu = cpu_baseline(wl, args.cpu_requests) if args.cpu_requests > 0 else None
     lens = wl.seq_lens
@@ -445,10 +450,10 @@ def run_insert(args):
 
 def _time_calls(calls, warmup, steps):
     """Warm up, time `steps` calls (rotating over `calls`) back to back on the
-    wall clock, then `steps` more with HIP events around each launch on the
-    current stream.  Returns (mean event ms per call, wall s of the first
-    pass); the events stay out of the wall-clock pass because each one idles
-    the GPU for a few microseconds."""
+    wall clock, then `steps` more in groups of KERNEL_GROUP with HIP events on
+    the current stream around each group.  Returns (mean event ms per call,
+    wall s of the first pass); no event sits between two timed calls, because
+    each one idles the GPU for a few microseconds."""
     stream = torch.cuda.current_stream(torch.device("cuda:0"))
     for i in range(warmup):
         calls[i % len(calls)]()
@@ -458,14 +463,16 @@ def _time_calls(calls, warmup, steps):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    n_groups = max(1, steps // KERNEL_GROUP)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        calls[i % len(calls)]()
-        ev[i][1].record(stream)
+          for _ in range(n_groups)]
+    for g in range(n_groups):
+        ev[g][0].record(stream)
+        for i in range(KERNEL_GROUP):
+            calls[i % len(calls)]()
+        ev[g][1].record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])), wall
+    return float(np.mean([a.elapsed_time(b) / KERNEL_GROUP for a, b in ev])), wall
 
 
 def _time_graph(calls, warmup, steps):
