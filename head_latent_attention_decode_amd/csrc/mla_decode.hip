@@ -237,11 +237,16 @@ __device__ __forceinline__ int window_block(const Params &p, PageWindow &win, in
 // which LDS stage a load targets and would otherwise wait for every load in
 // flight before each LDS read.  Completion is awaited explicitly with
 // wait_vmcnt; the kernels issue no other vector-memory operations while
-// tiles are in flight.
+// tiles are in flight.  The load is nontemporal (nt): each KV row is used once
+// by the workgroup that loads it.  On the 16-head kernel, whose rows no other
+// workgroup reads, this took long_context's split kernel from 114 to 102 us
+// (one interleaved run); on the role-split kernel's full tiles (dma16s), whose
+// rows the other head group's workgroup reads through the same L2, it changed
+// nothing measurable, so those keep the default policy.
 __device__ __forceinline__ void dma16(const void *src, LDS_AS void *dst)
 {
     const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
                  :
                  : "s"(m0), "v"(src)
                  : "memory", "m0");
