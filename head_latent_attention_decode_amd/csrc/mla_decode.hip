@@ -1436,7 +1436,10 @@ __global__ __launch_bounds__(256) void mla_concat_insert(
         const int c = (int)(i % 72);
         const bf16x8 v = c < 64 ? *(const bf16x8 *)(ql_nope + tn * kDV + 8 * c)
                                 : *(const bf16x8 *)(q_pe + tn * (kD - kDV) + 8 * (c - 64));
-        *(bf16x8 *)(q_out + tn * kD + 8 * c) = v;
+        // every store of this kernel is written once and read by a later one:
+        // nontemporal (64 tokens x 128 heads: 4.6 -> 3.9 us; 256 tokens: 12.7 ->
+        // 12.9 us)
+        __builtin_nontemporal_store(v, (bf16x8 *)(q_out + tn * kD + 8 * c));
         return;
     }
     i -= nq;
@@ -1450,7 +1453,7 @@ __global__ __launch_bounds__(256) void mla_concat_insert(
     if (!fp8) {
         const bf16x8 v = c < 64 ? *(const bf16x8 *)(kv_c + (long long)t * kDV + 8 * c)
                                 : *(const bf16x8 *)(k_pe + (long long)t * (kD - kDV) + 8 * (c - 64));
-        *(bf16x8 *)(cache + (slot * kD + 8 * c) * 2) = v;
+        __builtin_nontemporal_store(v, (bf16x8 *)(cache + (slot * kD + 8 * c) * 2));
         return;
     }
     // 16 elements 16c .. 16c+15 of the row, from kv_c (c < 32) or k_pe
@@ -1474,7 +1477,8 @@ __global__ __launch_bounds__(256) void mla_concat_insert(
         w[k] = (unsigned)r;
     }
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    *(u32x4 *)(cache + slot * kD + 16 * c) = u32x4{w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                (u32x4 *)(cache + slot * kD + 16 * c));
 }
 
 // ===========================================================================
@@ -1505,15 +1509,17 @@ __global__ __launch_bounds__(256) void mla_gather(
     const int blk = clamp_block(block_table[(long long)b * MB + pg], num_blocks);
     const long long row = (long long)blk * page_size + pos % page_size;
     __bf16 *d = dst + tok * kD;
+    // Each row is read once and written once: nontemporal loads and stores
+    // (dsv3's context, 262144 rows: 123.0 -> 120.1 us; the fp8 path unchanged).
     if (!fp8) {
         const bf16x8 *src = (const bf16x8 *)(cache + row * kD * 2);
         bf16x8 v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            v[j] = src[k + 18 * j];
+            v[j] = __builtin_nontemporal_load(src + k + 18 * j);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *(bf16x8 *)(d + 8 * (k + 18 * j)) = v[j];
+            __builtin_nontemporal_store(v[j], (bf16x8 *)(d + 8 * (k + 18 * j)));
         return;
     }
     // 16 codes at a time, decoded exactly to fp32, times the scale in fp32,
@@ -1524,7 +1530,7 @@ __global__ __launch_bounds__(256) void mla_gather(
     u32x4 v[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        v[j] = src[k + 18 * j];
+        v[j] = __builtin_nontemporal_load(src + k + 18 * j);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         bf16x8 r[2];
@@ -1541,8 +1547,8 @@ __global__ __launch_bounds__(256) void mla_gather(
             o[e + 2] = c[0];
             o[e + 3] = c[1];
         }
-        *(bf16x8 *)(d + 16 * (k + 18 * j)) = r[0];
-        *(bf16x8 *)(d + 16 * (k + 18 * j) + 8) = r[1];
+        __builtin_nontemporal_store(r[0], (bf16x8 *)(d + 16 * (k + 18 * j)));
+        __builtin_nontemporal_store(r[1], (bf16x8 *)(d + 16 * (k + 18 * j) + 8));
     }
 }
 
@@ -1580,11 +1586,15 @@ __global__ __launch_bounds__(256) void mla_merge_two(
         wp *= inv;
         ws *= inv;
     }
+    // The states are read once and the merged row written once: nontemporal
+    // loads and stores (T = 8192, N = 128, D = 128: 137.4 -> 126.7 us).
     if (live) {
         bf16x8 r = bf16x8{};
         if (M != -INFINITY) {
-            const bf16x8 p = *(const bf16x8 *)(prefix_out + rowi * D + 8 * c);
-            const bf16x8 q = *(const bf16x8 *)(suffix_out + rowi * D + 8 * c);
+            const bf16x8 p =
+                __builtin_nontemporal_load((const bf16x8 *)(prefix_out + rowi * D + 8 * c));
+            const bf16x8 q =
+                __builtin_nontemporal_load((const bf16x8 *)(suffix_out + rowi * D + 8 * c));
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const bf16x2 v = to_bf16x2(wp * (float)p[e] + ws * (float)q[e],
@@ -1593,7 +1603,7 @@ __global__ __launch_bounds__(256) void mla_merge_two(
                 r[e + 1] = v[1];
             }
         }
-        *(bf16x8 *)(out + rowi * D + 8 * c) = r;
+        __builtin_nontemporal_store(r, (bf16x8 *)(out + rowi * D + 8 * c));
     }
     __syncthreads();
     if (live && c == 0 && out_lse)
@@ -1704,7 +1714,11 @@ __global__ __launch_bounds__(256) void mla_head_mm(const __bf16 *__restrict__ x,
         const int r = s * kRowsPerSt + sr;
         const bf16x8 v = *(const LDS_AS bf16x8 *)(tile + r * kRow + 16 * sc);
         if (wrow0 + r < B)
-            *(bf16x8 *)(out + ((long long)(wrow0 + r) * N + n) * M + (long long)cb * kMb + 8 * sc) = v;
+            // written once and read by a later kernel: a nontemporal store
+            // (absorb at B = 64, N = 128: 6.5 -> 5.8 us; B = 256: 13.9 -> 13.0 us)
+            __builtin_nontemporal_store(
+                v, (bf16x8 *)(out + ((long long)(wrow0 + r) * N + n) * M + (long long)cb * kMb +
+                              8 * sc));
     }
 }
 
