@@ -42,7 +42,9 @@
  * Memory and threading contract, for every entry point:
  *   - Pointers marked "device" point to device memory allocated by the
  *     caller; the library allocates nothing, keeps no pointer after it
- *     returns, and holds no state: calls are reentrant.
+ *     returns, and holds no state: calls are reentrant.  The one exception
+ *     is mla_decode_noalloc, whose partials live in a static device array
+ *     (see its declaration).
  *   - Every call only enqueues kernels on `stream` and returns.  It performs
  *     no host<->device copy and never reads device data on the host, so the
  *     launch configuration depends only on the shape arguments and the calls
