@@ -699,7 +699,10 @@ def run_stream(args):
     volume (64 requests x 4096 rows x 1152 bytes = 302 MB), three buffers
     rotated so that no launch finds its data in the 256 MB Infinity Cache,
     for a sweep of grid sizes.  The decode kernels read each KV row once, so
-    this is the ceiling their KV stream can approach on this part."""
+    this is the ceiling their KV stream can approach on this part.  It also
+    reports one CU's request rate for L2-resident data (GB/s per CU), the
+    ceiling of a burst of tile loads, beside the per-CU share of the best
+    HBM stream."""
     from head_latent_attention_decode_amd import build as B
     if not B.PROBE_LIB.exists():
         raise RuntimeError(f"{B.PROBE_LIB} is missing: run __graft_entry__.build()")
@@ -732,8 +735,28 @@ def run_stream(args):
             ctypes.c_void_p(stream.cuda_stream))) for b in bufs]
         lms, _ = _time_calls(calls, args.warmup, args.steps)
         lds_gbs[f"{active}_waves_per_cu"] = round(nbytes / (lms * 1e-3) / 1e9, 1)
+    # a CU's request rate when every request hits L2 (8 windows of 256 KB, one
+    # per XCD slot), direct-to-LDS and into registers, 1 or 4 waves per CU:
+    # the ceiling of a tile-load burst, next to the per-CU share of the HBM stream
+    probe.l2_request_rate.restype = ctypes.c_int
+    probe.l2_request_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    win = torch.full((8 * 256 * 1024 // 4,), 1, dtype=torch.int32, device=dev)
+    n_batches = 600
+    l2_rate = {}
+    for lds, name in ((1, "direct_to_lds"), (0, "registers")):
+        for active in (1, 4):
+            calls = [lambda a=active, l=lds: probe.l2_request_rate(
+                ctypes.c_void_p(win.data_ptr()), n_batches, 256, a, l,
+                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))]
+            if calls[0]() != 0:
+                raise RuntimeError("l2_request_rate rejected its arguments")
+            rms, _ = _time_calls(calls, min(args.warmup, 50), min(args.steps, 200))
+            moved = 256 * active * n_batches * 8 * 1024
+            l2_rate[f"{name}_{active}_waves"] = round(moved / (rms * 1e-3) / 1e9 / 256, 2)
     best = min(results, key=lambda g: results[g][0])
     ms, wall = results[best]
+    l2_rate["hbm_stream_share"] = round(nbytes / (ms * 1e-3) / 1e9 / 256, 2)
     line = _op_line("attainable HBM read GB/s (plain streaming read, % of HBM peak)", nbytes, ms,
                     wall, args.steps, args.warmup, "hbm_stream_read_kernel",
                     f"stream: 302 MB read once per launch (the dsv3 KV volume), 3 buffers "
@@ -742,7 +765,8 @@ def run_stream(args):
                     {"best_grid": best,
                      "gbs_by_grid": {g: round(nbytes / (results[g][0] * 1e-3) / 1e9, 1)
                                      for g in grids},
-                     "direct_to_lds_gbs": lds_gbs})
+                     "direct_to_lds_gbs": lds_gbs,
+                     "l2_request_rate_gbs_per_cu": l2_rate})
     print(json.dumps(line), flush=True)
 
 
