@@ -22,8 +22,10 @@ event sits between two timed launches).
 Printed: one JSON line with the whole-call algorithmic bandwidth as `value`
 (GB/s: every KV row read once, plus q, out, lse, page-table entries and
 lengths), per-step time, TFLOP/s, the split kernel's roofline fraction and
-the fp64 CPU oracle timed on a sample of the same workload.  --op stream measures plain streaming reads of the dsv3 KV volume,
-the attainable-read reference for the decode kernels.
+the fp64 CPU oracle timed on a sample of the same workload, and the graphics
+and memory clocks that amd-smi reports during the timed passes (clocks are
+not locked on this part).  --op stream measures plain streaming reads of the
+dsv3 KV volume, the attainable-read reference for the decode kernels.
 """
 from __future__ import annotations
 
@@ -51,6 +53,90 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = ("decode attention GB/s and TFLOP/s (% of HBM/MFMA roofline); "
           "µs per B×N×Skv step")
 SPLIT_SRC = os.path.join(ROOT, "head_latent_attention_decode_amd", "csrc", "mla_decode.hip")
+
+
+class ClockSampler:
+    """The GPU's clock state while the timed steps run: a thread that reads
+    amd-smi's GPU metrics (current graphics clock of each XCD, memory clock,
+    clock lock) every 20 ms.  Clocks on this part are not locked by default
+    and follow power and temperature, so a step's time depends on them.  The
+    sample is None when amd-smi is unavailable or the device is ambiguous."""
+
+    def __init__(self, period_s=0.02):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.locked = None
+        self.mem_mhz = None
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._last_stamp = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:
+                raise RuntimeError(f"{len(handles)} GPUs visible to amd-smi")
+            self._smi, self._handle = amdsmi, handles[0]
+        except Exception as e:  # no amd-smi, or not one GPU: report no clocks
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        # the metrics table is refreshed by the firmware more slowly than it
+        # is read here: keep a table only when its timestamp has moved, and
+        # drop the first one, which may predate the timed work
+        stamp = m.get("system_clock_counter")
+        if stamp == self._last_stamp:
+            return
+        first = self._last_stamp is None
+        self._last_stamp = stamp
+        if first:
+            return
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int) and 0 < c < 65535]
+        if clks:
+            self.samples.append(sum(clks) / len(clks))
+        if isinstance(m.get("current_uclk"), int):
+            self.mem_mhz = m["current_uclk"]
+        if isinstance(m.get("gfxclk_lock_status"), int):
+            self.locked = bool(m["gfxclk_lock_status"])
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            try:
+                self._read()
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+
+    def __enter__(self):
+        if self._handle is not None:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def summary(self):
+        if self._handle is None:
+            return {"error": self.error}
+        # the firmware refreshes the table about once per 0.5-1 s, so a short
+        # run may see none
+        return {"gfx_mhz": [round(float(v), 0) for v in self.samples[:50]],
+                "mem_mhz": self.mem_mhz, "gfx_locked": self.locked,
+                "source": "amd-smi GPU metrics tables refreshed during the two timed passes "
+                          "(graphics clock: mean over the XCDs)"}
 
 
 def algorithmic_bytes(wl) -> int:
@@ -290,6 +376,7 @@ def main():
     K = args.steps
     first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clocks = ClockSampler().__enter__()
     t0 = time.perf_counter()
     first.record(stream)
     for i in range(K):
@@ -316,6 +403,7 @@ def main():
         for st in copies:
             st.merge()
     torch.cuda.synchronize()
+    clocks.__exit__(None, None, None)
     split_each = np.array([a.elapsed_time(b) / KERNEL_GROUP for a, b in ev])
     split_ms = float(split_each.mean())
     nbytes = algorithmic_bytes(wl)
@@ -369,6 +457,7 @@ def main():
                    "num_kv_splits": S, "page_size": wl.page_size,
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                    "input_copies_rotated": len(copies)},
+        "clocks": clocks.summary(),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
